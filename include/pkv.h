@@ -1,0 +1,171 @@
+/*
+ * pkv.h - attention over a block-paged KV cache on AMD MI355X (gfx950).
+ *
+ * C ABI of libpkv.so.  Every entry point takes plain pointers and sizes, enqueues
+ * its kernels on the caller's HIP stream and returns at once.  The library
+ * allocates no device memory and keeps no state between calls; it is safe to
+ * call from several threads on distinct buffers.
+ *
+ * Common conventions
+ *   - "device" pointers are HIP device (or managed) memory; every tensor is
+ *     contiguous and row-major in the shape given; every data pointer must be
+ *     16-byte aligned.
+ *   - dtype: PKV_F32 or PKV_BF16.  q, out, k_new, v_new and both pools share it.
+ *     All arithmetic accumulates in fp32; bf16 results are rounded to nearest even.
+ *   - KV pool (one per layer; the caller picks the layer by pointer):
+ *       k_cache, v_cache : [n_blocks, h_kv, 16, d_h]
+ *     A physical block holds 16 consecutive tokens of one sequence; inside a
+ *     block the layout is head-major, token, then channel.  This is the paged
+ *     pool of fixed 16-token blocks reached through a per-sequence block table
+ *     that the LLM Inference Server page describes (Optional Stretch
+ *     Challenges, "Paged KV-Cache Block Allocator"), and the "block table /
+ *     paged KV slots" box of the pipeline figure on the "LLM Inference Server
+ *     From Scratch" page (How it works).
+ *   - block_tables : int32 [n_seqs, max_blocks_per_seq]; token t of sequence s
+ *     lives in block block_tables[s][t / 16] at offset t % 16.  Entries past
+ *     ceil(context_len / 16) are never read.
+ *   - context_len counts every token of the sequence including the ones
+ *     appended this step (the cache is written first, then attended, as in the
+ *     LayerKVCache reference class of the LLM Inference Server page, Starter &
+ *     Verification Code Examples).
+ *   - Grouped-query attention (the "GQA" of the Attention Kernel box, pipeline
+ *     figure, From Scratch page): query head h reads KV head h / (h_q / h_kv).
+ *   - stream: a hipStream_t passed as void*; NULL is the null stream.
+ *
+ * Errors: every call returns a pkv_status.  Host-checkable argument errors are
+ * reported before any HIP call is made and nothing is enqueued.  Values that
+ * live in device memory (slots, table entries, lengths) are the caller's
+ * contract and are not read on the host unless the environment variable
+ * PKV_DEBUG=1 is set, in which case they are copied to the host (synchronising
+ * the stream) and checked; an out-of-range value then returns
+ * PKV_ERR_INVALID_ARG.  Without PKV_DEBUG the kernels still never touch memory
+ * outside the buffers described by the size arguments: an out-of-range slot is
+ * not written, an out-of-range block-table entry is read as block 0 and a
+ * context length is clamped to max_blocks_per_seq * 16; the results are then
+ * unspecified.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad device value (PKV_DEBUG) */
+  PKV_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (d_h, dtype) */
+  PKV_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
+  PKV_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} pkv_status;
+
+/* Human-readable name of a status code (static storage). */
+const char* pkv_status_string(int status);
+
+/*
+ * kv_append - write the K and V rows of T new tokens into their pool slots, in
+ * place.
+ *
+ * Defined by the pre-allocated cache that is updated in place at the current
+ * write position instead of being re-concatenated (LLM Inference Server page,
+ * Stage 1 "KV-Cache Engine", pre-allocation task, and its LayerKVCache class),
+ * with the write position given as a paged slot ("paged KV slots", pipeline
+ * figure of the From Scratch page).
+ *
+ *   k_new, v_new : device [T, h_kv, d_h]; row i is token i's K (resp. V).
+ *   slot_mapping : device int64 [T]; slot = physical_block * 16 + offset.  A
+ *                  negative slot skips that token (padding).  Two tokens with
+ *                  the same non-negative slot in one call is a caller error (the
+ *                  stored row is then one of them, unspecified which).
+ *   k_cache, v_cache : device pools, written in place; nothing else changes.
+ *   T >= 0 (T == 0 enqueues nothing), h_kv >= 1, d_h in {64, 128}, n_blocks >= 1.
+ * The copy is bit-exact.
+ */
+int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+              void* k_cache, void* v_cache,
+              int T, int h_kv, int d_h, int n_blocks, int dtype, void* stream);
+
+/*
+ * paged_decode_attention - one query token per sequence attends to its whole
+ * paged context.
+ *
+ * out[b, h, :] = sum_t softmax_t(scale * <q[b, h, :], K_b[t, h / g, :]>) V_b[t, h / g, :]
+ * over t < context_lens[b], g = h_q / h_kv.  This is the single-token decode
+ * step over the cached context of the LLM Inference Server page (Stage 1,
+ * prefill/decode task: a decode step feeds only the new token at start_pos =
+ * current length) for a continuous batch of variable-length sequences (From
+ * Scratch page, What you build).
+ *
+ *   out : device [B, h_q, d_h];  q : device [B, h_q, d_h]
+ *   k_cache, v_cache : device pools [n_blocks, h_kv, 16, d_h]
+ *   block_tables : device int32 [B, max_blocks_per_seq]
+ *   context_lens : device int32 [B], 0 <= context_lens[b] <= max_context_len.
+ *                  A context of length 0 gives an all-zero output row.
+ *   max_context_len : host int, an upper bound of context_lens,
+ *                  0 <= max_context_len <= max_blocks_per_seq * 16.
+ *   scale : the softmax scale (1/sqrt(d_h) for standard attention).
+ *   partition_tokens : 0 picks the split automatically; otherwise the context
+ *                  split length in tokens, a multiple of 16 in [16, 1024].
+ *   workspace : device scratch of at least pkv_decode_workspace_bytes(...) bytes
+ *                  for the same arguments (may be NULL when that is 0).  Its
+ *                  contents on entry do not matter.  The caller owns it and must
+ *                  not use it concurrently with the call.
+ * B == 0 enqueues nothing.  Requires h_q % h_kv == 0, d_h in {64, 128}.
+ */
+int paged_decode_attention(void* out, const void* q,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int B, int h_q, int h_kv, int d_h, int n_blocks,
+                           int max_blocks_per_seq, int max_context_len,
+                           float scale, int dtype, int partition_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Context split (tokens per partition) paged_decode_attention uses for these
+ * arguments; -1 on invalid arguments.  Host-only, no HIP call. */
+int pkv_decode_partition_tokens(int B, int h_q, int h_kv, int max_context_len,
+                                int partition_tokens);
+
+/* Workspace bytes paged_decode_attention needs for these arguments (0 when
+ * every sequence fits one partition).  Host-only, no HIP call.  Returns 0 for
+ * invalid arguments; the call itself then reports the error. */
+size_t pkv_decode_workspace_bytes(int B, int h_q, int h_kv, int d_h, int max_context_len,
+                                  int partition_tokens);
+
+/*
+ * paged_prefill_attention - causal attention of the new prompt tokens of S
+ * sequences over their paged contexts (chunked prefill).
+ *
+ * The prompt is processed in parallel (LLM Inference Server page, Stage 1,
+ * prefill/decode task: q_len = prompt length) with causal masking (Attention
+ * Kernel box of the pipeline figure and "What you build", From Scratch page).
+ * Query rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 are the n_s newest tokens
+ * of sequence s, at positions context_lens[s] - n_s .. context_lens[s] - 1; the
+ * query at position p attends to keys 0..p inclusive.  Their K/V must already
+ * be in the pool (kv_append first, on the same stream).
+ *
+ *   out, q : device [T_q, h_q, d_h], rows packed by sequence.
+ *   cu_seqlens_q : device int32 [S + 1], cu_seqlens_q[0] = 0,
+ *                  cu_seqlens_q[S] = T_q, n_s <= context_lens[s].
+ *   k_cache, v_cache, block_tables [S, max_blocks_per_seq], context_lens [S]:
+ *                  as for decode.
+ *   max_q_len : host int, an upper bound of every n_s.
+ * S == 0 or T_q == 0 enqueues nothing.  bf16 only (the QK^T and PV
+ * contractions run on bf16 matrix cores); PKV_F32 returns PKV_ERR_UNSUPPORTED.
+ */
+int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_q,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int S, int T_q, int max_q_len, int h_q, int h_kv, int d_h,
+                            int n_blocks, int max_blocks_per_seq, float scale, int dtype,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

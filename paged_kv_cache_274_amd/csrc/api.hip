@@ -1,0 +1,215 @@
+// C ABI of libpkv (declared in include/pkv.h): argument validation and dispatch.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "launch.h"
+#include "pkv.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(int dtype) {
+  if (dtype == PKV_F32) return 4;
+  if (dtype == PKV_BF16) return 2;
+  return 0;
+}
+
+bool debug_checks() {
+  static const bool on = [] {
+    const char* e = getenv("PKV_DEBUG");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+template <typename T>
+bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t stream) {
+  dst.resize(n);
+  if (n == 0) return true;
+  if (hipStreamSynchronize(stream) != hipSuccess) return false;
+  return hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost) == hipSuccess;
+}
+
+// PKV_DEBUG: context lengths and the block-table entries they reach.
+int debug_check_tables(const int32_t* tables, const int32_t* lens, int n_seqs, int max_blocks,
+                       int max_len, int n_blocks, hipStream_t stream) {
+  std::vector<int32_t> t, l;
+  if (!copy_to_host(l, lens, (size_t)n_seqs, stream)) return PKV_ERR_HIP;
+  if (!copy_to_host(t, tables, (size_t)n_seqs * max_blocks, stream)) return PKV_ERR_HIP;
+  for (int s = 0; s < n_seqs; ++s) {
+    if (l[s] < 0 || l[s] > max_len) return PKV_ERR_INVALID_ARG;
+    for (int j = 0; j < (l[s] + 15) / 16; ++j) {
+      const int32_t e = t[(size_t)s * max_blocks + j];
+      if (e < 0 || e >= n_blocks) return PKV_ERR_INVALID_ARG;
+    }
+  }
+  return PKV_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+  }
+  return "PKV_UNKNOWN_STATUS";
+}
+
+int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping, void* k_cache,
+              void* v_cache, int T, int h_kv, int d_h, int n_blocks, int dtype, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return PKV_ERR_INVALID_ARG;
+  if (T < 0 || h_kv <= 0 || n_blocks <= 0) return PKV_ERR_INVALID_ARG;
+  if (d_h != 64 && d_h != 128) return PKV_ERR_UNSUPPORTED;
+  if (T == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      ((uintptr_t)slot_mapping & 7u))
+    return PKV_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (debug_checks()) {
+    std::vector<int64_t> sl;
+    if (!copy_to_host(sl, slot_mapping, (size_t)T, s)) return PKV_ERR_HIP;
+    std::vector<char> seen((size_t)n_blocks * 16, 0);
+    for (int64_t v : sl) {
+      if (v < 0) continue;
+      if (v >= (int64_t)n_blocks * 16 || seen[(size_t)v]) return PKV_ERR_INVALID_ARG;
+      seen[(size_t)v] = 1;
+    }
+  }
+  return from_hip(pkv::launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, T, h_kv, d_h,
+                                        n_blocks, eb, s));
+}
+
+int pkv_decode_partition_tokens(int B, int h_q, int h_kv, int max_context_len,
+                                int partition_tokens) {
+  return pkv::decode_partition_tokens(B, h_q, h_kv, max_context_len, partition_tokens);
+}
+
+size_t pkv_decode_workspace_bytes(int B, int h_q, int h_kv, int d_h, int max_context_len,
+                                  int partition_tokens) {
+  const int P = pkv::decode_partition_tokens(B, h_q, h_kv, max_context_len, partition_tokens);
+  if (P <= 0 || d_h <= 0) return 0;
+  return pkv::decode_workspace_bytes(B, h_q, d_h, max_context_len, P);
+}
+
+int paged_decode_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, int B,
+                           int h_q, int h_kv, int d_h, int n_blocks, int max_blocks_per_seq,
+                           int max_context_len, float scale, int dtype, int partition_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (elem_bytes(dtype) == 0) return PKV_ERR_INVALID_ARG;
+  if (B < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0 || n_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0 ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * 16 || !isfinite(scale))
+    return PKV_ERR_INVALID_ARG;
+  if (d_h != 64 && d_h != 128) return PKV_ERR_UNSUPPORTED;
+  const int P = pkv::decode_partition_tokens(B, h_q, h_kv, max_context_len, partition_tokens);
+  if (P <= 0) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  const pkv::HeadChunks hc = pkv::head_chunks(h_q / h_kv);
+  if (B > 65535 || (int64_t)h_kv * hc.n_chunks > 65535) return PKV_ERR_UNSUPPORTED;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u))
+    return PKV_ERR_INVALID_ARG;
+  const size_t need = pkv::decode_workspace_bytes(B, h_q, d_h, max_context_len, P);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return PKV_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (debug_checks()) {
+    const int rc = debug_check_tables(block_tables, context_lens, B, max_blocks_per_seq,
+                                      max_context_len, n_blocks, s);
+    if (rc != PKV_OK) return rc;
+  }
+  pkv::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_partitions = max(1, pkv::decode_num_partitions(max_context_len, P));
+  a.ws_acc = (float*)workspace;
+  a.ws_ml = need ? (float*)workspace + (size_t)B * h_q * a.num_partitions * d_h : nullptr;
+  a.B = B;
+  a.h_q = h_q;
+  a.h_kv = h_kv;
+  a.g = h_q / h_kv;
+  a.n_chunks = hc.n_chunks;
+  a.n_blocks = n_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.partition_tokens = P;
+  a.scale_log2 = scale * kLog2e;
+  return from_hip(pkv::launch_decode(a, d_h, dtype == PKV_BF16, s));
+}
+
+int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_q,
+                            const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int S, int T_q, int max_q_len, int h_q,
+                            int h_kv, int d_h, int n_blocks, int max_blocks_per_seq, float scale,
+                            int dtype, void* stream) {
+  if (elem_bytes(dtype) == 0) return PKV_ERR_INVALID_ARG;
+  if (S < 0 || T_q < 0 || max_q_len < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0 ||
+      n_blocks <= 0 || max_blocks_per_seq <= 0 || !isfinite(scale))
+    return PKV_ERR_INVALID_ARG;
+  if (d_h != 64 && d_h != 128) return PKV_ERR_UNSUPPORTED;
+  if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (S == 0 || T_q == 0 || max_q_len == 0) return PKV_OK;
+  if (S > 65535 || h_kv > 65535) return PKV_ERR_UNSUPPORTED;
+  if (!out || !q || !cu_seqlens_q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u) ||
+      ((uintptr_t)cu_seqlens_q & 3u))
+    return PKV_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (debug_checks()) {
+    std::vector<int32_t> cu, l;
+    if (!copy_to_host(cu, cu_seqlens_q, (size_t)S + 1, s)) return PKV_ERR_HIP;
+    if (!copy_to_host(l, context_lens, (size_t)S, s)) return PKV_ERR_HIP;
+    if (cu[0] != 0 || cu[S] != T_q) return PKV_ERR_INVALID_ARG;
+    for (int i = 0; i < S; ++i) {
+      const int n = cu[i + 1] - cu[i];
+      if (n < 0 || n > max_q_len || n > l[i]) return PKV_ERR_INVALID_ARG;
+    }
+    const int rc = debug_check_tables(block_tables, context_lens, S, max_blocks_per_seq,
+                                      max_blocks_per_seq * 16, n_blocks, s);
+    if (rc != PKV_OK) return rc;
+  }
+  pkv::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.S = S;
+  a.T_q = T_q;
+  a.max_q_len = max_q_len;
+  a.h_q = h_q;
+  a.h_kv = h_kv;
+  a.g = h_q / h_kv;
+  a.n_blocks = n_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale_log2 = scale * kLog2e;
+  return from_hip(pkv::launch_prefill_bf16(a, d_h, s));
+}
+
+}  // extern "C"

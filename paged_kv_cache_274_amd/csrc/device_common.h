@@ -1,0 +1,92 @@
+// Device helpers shared by the gfx950 kernels of libpkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kBlock = 16;      // tokens per physical KV block
+constexpr int kWave = 64;       // CDNA wavefront width
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// bf16 storage type: raw 16-bit pattern.
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t packed) {
+  return __uint_as_float(packed << 16);
+}
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t packed) {
+  return __uint_as_float(packed & 0xffff0000u);
+}
+
+// fp32 -> bf16 with round-to-nearest-even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Lane permutations inside a row of 16 lanes through DPP (no LDS traffic).
+// quad_perm [1,0,3,2] = lane ^ 1; [2,3,0,1] = lane ^ 2; row_half_mirror maps
+// lane i to 7 - i inside each half-row; row_mirror maps lane i to 15 - i;
+// row_ror:n rotates the 16 lanes of a row by n.
+enum : int {
+  kDppXor1 = 0xB1,
+  kDppXor2 = 0x4E,
+  kDppRowHalfMirror = 0x141,
+  kDppRowMirror = 0x140,
+  kDppRowRor4 = 0x124,
+  kDppRowRor8 = 0x128,
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of N consecutive lanes (N in 1, 2, 4, 8, 16); every
+// lane of a group receives the group total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<kDppXor1>(x);
+  if constexpr (N >= 4) x += dpp<kDppXor2>(x);
+  if constexpr (N >= 8) x += dpp<kDppRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
+  return x;
+}
+
+// Combine lanes that share (lane mod N) across the whole wave, N in 4, 8, 16,
+// 32, 64: every lane receives the sum (max) over the 64/N lanes of its class.
+template <int N>
+__device__ __forceinline__ float class_sum(float x) {
+  if constexpr (N <= 4) x += dpp<kDppRowRor4>(x);
+  if constexpr (N <= 8) x += dpp<kDppRowRor8>(x);
+  if constexpr (N <= 16) x += __shfl_xor(x, 16);
+  if constexpr (N <= 32) x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float class_max(float x) {
+  if constexpr (N <= 4) x = fmaxf(x, dpp<kDppRowRor4>(x));
+  if constexpr (N <= 8) x = fmaxf(x, dpp<kDppRowRor8>(x));
+  if constexpr (N <= 16) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (N <= 32) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pkv

@@ -1,0 +1,181 @@
+"""Thin ctypes binding of libpkv.so (include/pkv.h), same call names.
+
+Argument marshalling only: shapes and dtypes are checked, torch tensors are
+passed as device pointers together with torch's current HIP stream, and every
+step of the computation runs in the library's HIP kernels.  There is no
+fallback: if ``libpkv.so`` is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_F32, PKV_BF16 = 0, 1
+_DTYPE = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
+EXPORTED = ("kv_append", "paged_decode_attention", "paged_prefill_attention",
+            "pkv_decode_workspace_bytes", "pkv_decode_partition_tokens", "pkv_status_string")
+
+_lib = None
+
+
+class PkvError(RuntimeError):
+    def __init__(self, what: str, status: int):
+        super().__init__(f"{what} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpkv.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m paged_kv_cache_274_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64p, i32p = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
+    L.pkv_status_string.argtypes = [i32]
+    L.pkv_status_string.restype = ctypes.c_char_p
+    L.kv_append.argtypes = [vp, vp, i64p, vp, vp, i32, i32, i32, i32, i32, vp]
+    L.kv_append.restype = i32
+    L.pkv_decode_partition_tokens.argtypes = [i32, i32, i32, i32, i32]
+    L.pkv_decode_partition_tokens.restype = i32
+    L.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.pkv_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.paged_decode_attention.argtypes = [vp, vp, vp, vp, i32p, i32p, i32, i32, i32, i32, i32, i32,
+                                         i32, ctypes.c_float, i32, i32, vp, ctypes.c_size_t, vp]
+    L.paged_decode_attention.restype = i32
+    L.paged_prefill_attention.argtypes = [vp, vp, i32p, vp, vp, i32p, i32p, i32, i32, i32, i32, i32,
+                                          i32, i32, i32, ctypes.c_float, i32, vp]
+    L.paged_prefill_attention.restype = i32
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().pkv_status_string(int(status)).decode()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(*ts: torch.Tensor):
+    dev = ts[0].device
+    for t in ts:
+        _need(t.is_cuda and t.device == dev, "all tensors must be on the same GPU")
+        _need(t.is_contiguous(), "all tensors must be contiguous")
+
+
+def _pool_shape(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    _need(k_cache.dim() == 4 and k_cache.shape[2] == 16, "pool must be [n_blocks, h_kv, 16, d_h]")
+    _need(v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype, "K/V pools differ")
+    n_blocks, h_kv, _, d = k_cache.shape
+    return int(n_blocks), int(h_kv), int(d)
+
+
+def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+              k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Write new K/V rows [T, h_kv, d_h] into pool slots (int64 [T]), in place."""
+    n_blocks, h_kv, d = _pool_shape(k_cache, v_cache)
+    _dev(k_new, v_new, slot_mapping, k_cache, v_cache)
+    _need(k_new.dim() == 3 and k_new.shape[1:] == (h_kv, d) and v_new.shape == k_new.shape,
+          "k_new/v_new must be [T, h_kv, d_h]")
+    _need(k_new.dtype == k_cache.dtype == v_new.dtype, "dtype mismatch")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (k_new.shape[0],),
+          "slot_mapping must be int64 [T]")
+    _need(k_cache.dtype in _DTYPE, f"unsupported dtype {k_cache.dtype}")
+    rc = lib().kv_append(k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(),
+                         k_cache.data_ptr(), v_cache.data_ptr(), int(k_new.shape[0]), h_kv, d,
+                         n_blocks, _DTYPE[k_cache.dtype], _stream(k_cache))
+    if rc != 0:
+        raise PkvError("kv_append", rc)
+
+
+def decode_partition_tokens(B: int, h_q: int, h_kv: int, max_context_len: int,
+                            partition_tokens: int = 0) -> int:
+    return int(lib().pkv_decode_partition_tokens(B, h_q, h_kv, max_context_len, partition_tokens))
+
+
+def decode_workspace_bytes(B: int, h_q: int, h_kv: int, d_h: int, max_context_len: int,
+                           partition_tokens: int = 0) -> int:
+    return int(lib().pkv_decode_workspace_bytes(B, h_q, h_kv, d_h, max_context_len,
+                                                 partition_tokens))
+
+
+def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           max_context_len: int, scale: Optional[float] = None,
+                           partition_tokens: int = 0, out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Single-token decode over paged K/V.  q, out: [B, h_q, d_h]."""
+    n_blocks, h_kv, d = _pool_shape(k_cache, v_cache)
+    _need(q.dim() == 3 and q.shape[2] == d and q.dtype == k_cache.dtype, "q must be [B, h_q, d_h]")
+    B, h_q = int(q.shape[0]), int(q.shape[1])
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == B, "block_tables must be int32 [B, max_blocks]")
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (B,),
+          "context_lens must be int32 [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _dev(q, k_cache, v_cache, block_tables, context_lens, out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_bytes = decode_workspace_bytes(B, h_q, h_kv, d, int(max_context_len), partition_tokens)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().paged_decode_attention(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), B, h_q, h_kv, d, n_blocks,
+        int(block_tables.shape[1]), int(max_context_len), float(scale), _DTYPE[q.dtype],
+        int(partition_tokens), ws_ptr, ws_len, _stream(q))
+    if rc != 0:
+        raise PkvError("paged_decode_attention", rc)
+    return out
+
+
+def paged_prefill_attention(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor, block_tables: torch.Tensor,
+                            context_lens: torch.Tensor, max_q_len: int,
+                            scale: Optional[float] = None,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal chunked prefill over paged K/V.  q, out: packed [T_q, h_q, d_h]."""
+    n_blocks, h_kv, d = _pool_shape(k_cache, v_cache)
+    _need(q.dim() == 3 and q.shape[2] == d and q.dtype == k_cache.dtype,
+          "q must be [T_q, h_q, d_h]")
+    T_q, h_q = int(q.shape[0]), int(q.shape[1])
+    S = int(context_lens.shape[0])
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.shape == (S + 1,),
+          "cu_seqlens_q must be int32 [S + 1]")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == S, "block_tables must be int32 [S, max_blocks]")
+    _need(context_lens.dtype == torch.int32, "context_lens must be int32 [S]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _dev(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rc = lib().paged_prefill_attention(
+        out.data_ptr(), q.data_ptr(), cu_seqlens_q.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), S, T_q,
+        int(max_q_len), h_q, h_kv, d, n_blocks, int(block_tables.shape[1]), float(scale),
+        _DTYPE[q.dtype], _stream(q))
+    if rc != 0:
+        raise PkvError("paged_prefill_attention", rc)
+    return out

@@ -1,0 +1,117 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/pkv.h, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_274_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000      # a 16-byte aligned non-null address that is never dereferenced
+MISALIGNED = 0x10008
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("kv_append", "paged_decode_attention", "paged_prefill_attention"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ops.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) == set(ops.EXPORTED)
+
+
+def test_status_strings():
+    assert [ops.status_string(i) for i in range(5)] == [
+        "PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP"]
+    assert ops.status_string(99) == "PKV_UNKNOWN_STATUS"
+
+
+def _append(**kw):
+    a = dict(k_new=FAKE, v_new=FAKE, slots=FAKE, kc=FAKE, vc=FAKE, T=4, h_kv=2, d=64, nb=8, dt=1)
+    a.update(kw)
+    return ops.lib().kv_append(a["k_new"], a["v_new"], a["slots"], a["kc"], a["vc"], a["T"],
+                               a["h_kv"], a["d"], a["nb"], a["dt"], None)
+
+
+def test_kv_append_validation():
+    assert _append(dt=7) == 1
+    assert _append(T=-1) == 1
+    assert _append(h_kv=0) == 1
+    assert _append(nb=0) == 1
+    assert _append(d=96) == 2
+    assert _append(k_new=None) == 1
+    assert _append(vc=MISALIGNED) == 1
+    assert _append(slots=FAKE + 4) == 1
+    assert _append(T=0, k_new=None, v_new=None) == 0   # empty: nothing enqueued
+
+
+def _decode(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, tbl=FAKE, lens=FAKE, B=4, h_q=8, h_kv=2, d=128,
+             nb=64, mb=16, maxc=256, scale=0.1, dt=1, P=0, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return ops.lib().paged_decode_attention(
+        a["out"], a["q"], a["kc"], a["vc"], a["tbl"], a["lens"], a["B"], a["h_q"], a["h_kv"],
+        a["d"], a["nb"], a["mb"], a["maxc"], a["scale"], a["dt"], a["P"], a["ws"], a["ws_bytes"],
+        None)
+
+
+def test_decode_validation():
+    assert _decode(dt=3) == 1
+    assert _decode(h_q=6, h_kv=4) == 1
+    assert _decode(maxc=16 * 16 + 1) == 1
+    assert _decode(B=-1) == 1
+    assert _decode(d=80) == 2
+    assert _decode(q=None) == 1
+    assert _decode(out=MISALIGNED) == 1
+    assert _decode(P=24) == 1
+    assert _decode(P=2048) == 1
+    assert _decode(scale=float("nan")) == 1
+    assert _decode(ws=None, P=16) == 3
+    need = ops.decode_workspace_bytes(4, 8, 2, 128, 256, 16)
+    assert need > 0
+    assert _decode(P=16, ws_bytes=need - 1) == 3
+    assert _decode(B=0, out=None, q=None) == 0
+
+
+def _prefill(**kw):
+    a = dict(out=FAKE, q=FAKE, cu=FAKE, kc=FAKE, vc=FAKE, tbl=FAKE, lens=FAKE, S=2, T_q=10,
+             mq=8, h_q=14, h_kv=2, d=64, nb=64, mb=16, scale=0.125, dt=1)
+    a.update(kw)
+    return ops.lib().paged_prefill_attention(
+        a["out"], a["q"], a["cu"], a["kc"], a["vc"], a["tbl"], a["lens"], a["S"], a["T_q"],
+        a["mq"], a["h_q"], a["h_kv"], a["d"], a["nb"], a["mb"], a["scale"], a["dt"], None)
+
+
+def test_prefill_validation():
+    assert _prefill(dt=0) == 2          # fp32 prefill is not provided
+    assert _prefill(dt=5) == 1
+    assert _prefill(h_q=15) == 1
+    assert _prefill(d=32) == 2
+    assert _prefill(cu=None) == 1
+    assert _prefill(q=MISALIGNED) == 1
+    assert _prefill(S=0, out=None) == 0
+    assert _prefill(T_q=0, out=None) == 0
+
+
+@pytest.mark.parametrize("B,h_q,h_kv,maxc", [(64, 32, 8, 4096), (8, 32, 8, 8192), (8, 32, 8, 512),
+                                              (60, 14, 2, 2048), (2, 4, 2, 40), (1, 64, 4, 100000)])
+def test_partition_heuristic(B, h_q, h_kv, maxc):
+    P = ops.decode_partition_tokens(B, h_q, h_kv, maxc)
+    assert 64 <= P <= 1024 and (P & (P - 1)) == 0
+    nparts = -(-maxc // P)
+    ws = ops.decode_workspace_bytes(B, h_q, h_kv, 128, maxc)
+    assert ws == (0 if nparts <= 1 else B * h_q * nparts * (128 + 2) * 4)
+    assert ops.decode_partition_tokens(B, h_q, h_kv, maxc, 48) == 48
+    assert ops.decode_partition_tokens(B, h_q, h_kv, maxc, 40) == -1

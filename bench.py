@@ -74,8 +74,7 @@ class Resident:
         self.pools = [(w.k_cache.to(dev), w.v_cache.to(dev)) for _ in range(copies)]
         self.out = torch.empty_like(self.q)
         self.pre_out = torch.empty_like(self.pre_q)
-        self.P = ops.decode_partition_tokens(w.B, w.h_q, w.h_kv, w.dec_max_context_len)
-        nbytes = ops.decode_workspace_bytes(w.B, w.h_q, w.h_kv, w.d, w.dec_max_context_len)
+        nbytes = ops.decode_workspace_bytes(w.B, w.h_q, w.h_kv, w.d, w.dec_max_context_len, w.dtype)
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
 
     def append(self, i: int):
@@ -217,13 +216,13 @@ def main(argv=None):
             "context_tokens": int(w3.dec_context_lens.sum()),
             "kv_bytes_per_step": kvb,
             "n_blocks": w3.n_blocks,
-            "partition_tokens": ops.decode_partition_tokens(w3.B, w3.h_q, w3.h_kv,
-                                                            w3.dec_max_context_len),
+            "num_splits": ops.decode_num_splits(w3.B, w3.h_q, w3.h_kv, w3.d,
+                                                w3.dec_max_context_len, w3.dtype),
             "pool_copies_rotated": args.copies,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_attention (split-context pass + merge pass)",
+            "kernel": "paged_decode_attention (split pass + combine pass)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -109,12 +109,15 @@ int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
  *   max_context_len : host int, an upper bound of context_lens,
  *                  0 <= max_context_len <= max_blocks_per_seq * 16.
  *   scale : the softmax scale (1/sqrt(d_h) for standard attention).
- *   partition_tokens : 0 picks the split automatically; otherwise the context
- *                  split length in tokens, a multiple of 16 in [16, 1024].
+ *   num_splits : 0 picks the split automatically (one range per wavefront the
+ *                  device holds at once, capped by the work); otherwise the
+ *                  number of equal ranges, 1 .. 65536, that the blocks of all
+ *                  (sequence, KV head) pairs, laid end to end, are cut into.
+ *                  Results agree across splits to rounding.
  *   workspace : device scratch of at least pkv_decode_workspace_bytes(...) bytes
- *                  for the same arguments (may be NULL when that is 0).  Its
- *                  contents on entry do not matter.  The caller owns it and must
- *                  not use it concurrently with the call.
+ *                  for the same arguments, 16-byte aligned.  Its contents on
+ *                  entry do not matter.  The caller owns it and must not use it
+ *                  concurrently with the call.
  * B == 0 enqueues nothing.  Requires h_q % h_kv == 0, d_h in {64, 128}.
  */
 int paged_decode_attention(void* out, const void* q,
@@ -122,19 +125,21 @@ int paged_decode_attention(void* out, const void* q,
                            const int32_t* block_tables, const int32_t* context_lens,
                            int B, int h_q, int h_kv, int d_h, int n_blocks,
                            int max_blocks_per_seq, int max_context_len,
-                           float scale, int dtype, int partition_tokens,
+                           float scale, int dtype, int num_splits,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Context split (tokens per partition) paged_decode_attention uses for these
- * arguments; -1 on invalid arguments.  Host-only, no HIP call. */
-int pkv_decode_partition_tokens(int B, int h_q, int h_kv, int max_context_len,
-                                int partition_tokens);
+/* Number of splits paged_decode_attention uses for these arguments; -1 on
+ * invalid arguments.  With num_splits == 0 it queries the current device's
+ * occupancy for the decode kernel (2048 wavefronts are assumed when no device
+ * can be queried). */
+int pkv_decode_num_splits(int B, int h_q, int h_kv, int d_h, int max_context_len, int dtype,
+                          int num_splits);
 
-/* Workspace bytes paged_decode_attention needs for these arguments (0 when
- * every sequence fits one partition).  Host-only, no HIP call.  Returns 0 for
- * invalid arguments; the call itself then reports the error. */
+/* Workspace bytes paged_decode_attention needs for these arguments: enough for
+ * the largest automatic split.  Host-only, no HIP call.  Returns 0 for invalid
+ * arguments; the call itself then reports the error. */
 size_t pkv_decode_workspace_bytes(int B, int h_q, int h_kv, int d_h, int max_context_len,
-                                  int partition_tokens);
+                                  int dtype, int num_splits);
 
 /*
  * paged_prefill_attention - causal attention of the new prompt tokens of S

@@ -7,7 +7,7 @@ memory and the current stream.  ``workloads`` builds seeded synthetic inputs.
 """
 
 __all__ = ["kv_append", "paged_decode_attention", "paged_prefill_attention",
-           "decode_workspace_bytes", "decode_partition_tokens"]
+           "decode_workspace_bytes", "decode_num_splits"]
 
 
 def __getattr__(name):

@@ -95,42 +95,61 @@ int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                                         n_blocks, eb, s));
 }
 
-int pkv_decode_partition_tokens(int B, int h_q, int h_kv, int max_context_len,
-                                int partition_tokens) {
-  return pkv::decode_partition_tokens(B, h_q, h_kv, max_context_len, partition_tokens);
+static bool decode_shape_ok(int B, int h_q, int h_kv, int max_context_len, int num_splits) {
+  return B >= 0 && h_q > 0 && h_kv > 0 && h_q % h_kv == 0 && max_context_len >= 0 &&
+         num_splits >= 0 && num_splits <= pkv::kMaxSplits;
+}
+
+// Automatic split count: one range per wavefront the device holds at once.
+static int auto_splits(int B, int h_q, int h_kv, int d_h, int max_context_len, bool bf16) {
+  const int gc = pkv::head_chunks(h_q / h_kv, d_h, bf16).per_chunk;
+  int waves = pkv::decode_resident_waves(d_h, bf16, gc);
+  if (waves <= 0) waves = 2048;
+  const int64_t bound = pkv::decode_split_bound(B, h_q, h_kv, d_h, bf16, max_context_len, 0);
+  return (int)(waves < bound ? waves : bound);
+}
+
+int pkv_decode_num_splits(int B, int h_q, int h_kv, int d_h, int max_context_len, int dtype,
+                          int num_splits) {
+  if (!decode_shape_ok(B, h_q, h_kv, max_context_len, num_splits) || elem_bytes(dtype) == 0 ||
+      (d_h != 64 && d_h != 128))
+    return -1;
+  if (num_splits > 0) return num_splits;
+  return auto_splits(B, h_q, h_kv, d_h, max_context_len, dtype == PKV_BF16);
 }
 
 size_t pkv_decode_workspace_bytes(int B, int h_q, int h_kv, int d_h, int max_context_len,
-                                  int partition_tokens) {
-  const int P = pkv::decode_partition_tokens(B, h_q, h_kv, max_context_len, partition_tokens);
-  if (P <= 0 || d_h <= 0) return 0;
-  return pkv::decode_workspace_bytes(B, h_q, d_h, max_context_len, P);
+                                  int dtype, int num_splits) {
+  if (!decode_shape_ok(B, h_q, h_kv, max_context_len, num_splits) || d_h <= 0 ||
+      elem_bytes(dtype) == 0)
+    return 0;
+  return pkv::decode_workspace_bytes(B, h_q, h_kv, d_h, dtype == PKV_BF16, max_context_len,
+                                     num_splits);
 }
 
 int paged_decode_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_tables, const int32_t* context_lens, int B,
                            int h_q, int h_kv, int d_h, int n_blocks, int max_blocks_per_seq,
-                           int max_context_len, float scale, int dtype, int partition_tokens,
+                           int max_context_len, float scale, int dtype, int num_splits,
                            void* workspace, size_t workspace_bytes, void* stream) {
   if (elem_bytes(dtype) == 0) return PKV_ERR_INVALID_ARG;
-  if (B < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0 || n_blocks <= 0 ||
-      max_blocks_per_seq <= 0 || max_context_len < 0 ||
-      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * 16 || !isfinite(scale))
+  if (!decode_shape_ok(B, h_q, h_kv, max_context_len, num_splits) || n_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * 16 ||
+      !isfinite(scale))
     return PKV_ERR_INVALID_ARG;
   if (d_h != 64 && d_h != 128) return PKV_ERR_UNSUPPORTED;
-  const int P = pkv::decode_partition_tokens(B, h_q, h_kv, max_context_len, partition_tokens);
-  if (P <= 0) return PKV_ERR_INVALID_ARG;
   if (B == 0) return PKV_OK;
-  const pkv::HeadChunks hc = pkv::head_chunks(h_q / h_kv);
-  if (B > 65535 || (int64_t)h_kv * hc.n_chunks > 65535) return PKV_ERR_UNSUPPORTED;
+  const bool bf16 = dtype == PKV_BF16;
+  const pkv::HeadChunks hc = pkv::head_chunks(h_q / h_kv, d_h, bf16);
+  if ((int64_t)B * h_kv * hc.n_chunks > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
       ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u))
     return PKV_ERR_INVALID_ARG;
-  const size_t need = pkv::decode_workspace_bytes(B, h_q, d_h, max_context_len, P);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
-    return PKV_ERR_WORKSPACE;
+  const size_t need =
+      pkv::decode_workspace_bytes(B, h_q, h_kv, d_h, bf16, max_context_len, num_splits);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKV_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (debug_checks()) {
     const int rc = debug_check_tables(block_tables, context_lens, B, max_blocks_per_seq,
@@ -144,19 +163,18 @@ int paged_decode_attention(void* out, const void* q, const void* k_cache, const 
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.num_partitions = max(1, pkv::decode_num_partitions(max_context_len, P));
-  a.ws_acc = (float*)workspace;
-  a.ws_ml = need ? (float*)workspace + (size_t)B * h_q * a.num_partitions * d_h : nullptr;
+  a.ws = (float*)workspace;
   a.B = B;
   a.h_q = h_q;
   a.h_kv = h_kv;
   a.g = h_q / h_kv;
   a.n_chunks = hc.n_chunks;
+  a.gc = hc.per_chunk;
   a.n_blocks = n_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
-  a.partition_tokens = P;
+  a.num_splits = num_splits > 0 ? num_splits : auto_splits(B, h_q, h_kv, d_h, max_context_len, bf16);
   a.scale_log2 = scale * kLog2e;
-  return from_hip(pkv::launch_decode(a, d_h, dtype == PKV_BF16, s));
+  return from_hip(pkv::launch_decode(a, d_h, bf16, s));
 }
 
 int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_q,

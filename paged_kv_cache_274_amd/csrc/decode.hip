@@ -1,4 +1,4 @@
-// Split-context paged decode attention for gfx950.
+// Paged decode attention for gfx950: wave-level even split of the whole batch.
 //
 // Single-token decode over the cached context of a continuous batch of
 // variable-length sequences (LLM Inference Server page, Stage 1 prefill/decode
@@ -6,28 +6,37 @@
 // and 16-token blocks behind a per-sequence block table (Paged KV-Cache Block
 // Allocator stretch challenge; Block Manager box of the pipeline figure).
 // Decode is bound by reading the KV cache from HBM ("What You Will Build",
-// LLM Inference Server page), so the design goal is streaming every K/V byte
-// exactly once at full bandwidth:
+// LLM Inference Server page): the design streams every K/V byte once, with the
+// whole chip busy from the first to the last cycle.
 //
-//  * Work unit = (sequence b, KV head, chunk of <= 8 query heads of its GQA
-//    group, context partition).  A partition of P tokens is split block by block
-//    over the 4 wavefronts of the workgroup; each K/V block of a KV head is read
-//    once for every query head of the chunk.
-//  * A wavefront streams whole 16-token blocks straight into VGPRs with 16-byte
-//    loads; the next block's loads are in flight while the current block is
-//    used.  A token row is covered by LPT = row_bytes / 32 adjacent lanes, so
-//    one load instruction reads contiguous half-rows of 64 / LPT tokens.
-//  * q.K partial sums are combined across the LPT lanes of a token with DPP row
-//    permutations (no LDS).  bf16 products use v_dot2_f32_bf16.
-//  * Online softmax in base 2 (scale * log2(e) folded into the score).  Every
-//    lane keeps its own running reference max, sum and fp32 accumulators for
-//    the tokens it owns; the reference only moves when a score exceeds it by
-//    more than 2^8, so rescaling the accumulators is rare.  The per-lane states
-//    are merged exactly (log-sum-exp) at the end: across lanes with DPP/
-//    shuffles, across the 4 waves through LDS, and across partitions by the
-//    second kernel.
-//  * A context that fits one partition is normalised and stored by the first
-//    kernel; the merge kernel skips it.
+// Work decomposition
+//  * A segment is (sequence b, KV head, chunk of <= 8 query heads of its GQA
+//    group); it owns the ceil(L_b / 16) blocks of that KV head.  All segments'
+//    blocks are laid end to end (sequence-major) and the line is cut into
+//    num_splits equal contiguous ranges, one per wavefront.  With num_splits =
+//    the number of wavefronts the chip holds at once, every wave starts at once,
+//    does the same number of blocks whatever the length mix, and finishes at
+//    once; there is no per-partition prologue or tail.
+//  * A wave walks its range block by block, crossing segment boundaries.  Each
+//    K/V block of a KV head is read once for all query heads of the chunk.
+//    A segment finished inside one wave is normalised and stored directly; a
+//    segment cut by a range boundary leaves an unnormalised partial state
+//    (max, sum, accumulator) in the workspace, at most two per wave, and the
+//    combine kernel merges them with the exact log-sum-exp rule.
+//
+// Inside a wave
+//  * 8 adjacent lanes cover one token row (16-byte loads), so a load
+//    instruction reads 8 tokens x 128 contiguous bytes and a block takes two
+//    passes.  The next block's loads are in flight while the current one is used.
+//  * q.K partial sums are combined across the 8 lanes of a token by DPP row
+//    permutations (no LDS).  bf16 products use v_dot2_f32_bf16; for P.V the
+//    two tokens a lane holds are paired so that one v_dot2 adds both
+//    (weights rounded to bf16, accumulation in fp32).  fp32 inputs use fp32 FMAs.
+//  * Online softmax in base 2 (scale * log2(e) folded into the score).  Each
+//    lane keeps its own reference max, sum and accumulators for its tokens; the
+//    reference only moves when a score exceeds it by more than 2^8, so the
+//    accumulators are rarely rescaled.  The lanes' states are merged exactly at
+//    the end of each segment piece.
 #include <type_traits>
 
 #include "device_common.h"
@@ -35,127 +44,156 @@
 
 namespace pkv {
 
-constexpr int kDecodeWaves = 4;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
+#ifndef PKV_DECODE_DEPTH
+#define PKV_DECODE_DEPTH 2
+#endif
+constexpr int kDepth = PKV_DECODE_DEPTH;  // K/V blocks a wave holds in registers
+#ifndef PKV_DECODE_WAVES_PER_SIMD
+#define PKV_DECODE_WAVES_PER_SIMD 2
+#endif
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// Lane mapping.  A token row of D elements is covered by kLPT adjacent lanes,
+// each holding kVPL 16-byte vectors of it; one load instruction covers kTPW
+// tokens and a 16-token block takes kPasses passes.  bf16 rows of 128 channels
+// use 16 lanes (8 channels per lane) so that the per-lane accumulators and
+// query words stay small enough for three wavefronts per SIMD; other rows use 8.
 template <typename T, int D>
 struct DecodeShape {
   static constexpr int kElem = sizeof(T);
   static constexpr int kRowVec = D * kElem / 16;   // 16-byte vectors per token row
-  static constexpr int kLPT = kRowVec / 2;         // lanes per token row (two vectors each)
+  static constexpr int kLPT = (kElem == 2 && kRowVec >= 16) ? 16 : 8;
+  static constexpr int kVPL = kRowVec / kLPT;
   static constexpr int kEPV = 16 / kElem;          // elements per vector
-  static constexpr int kEPL = 2 * kEPV;            // elements a lane holds of one token
+  static constexpr int kEPL = kVPL * kEPV;         // elements a lane holds of one token
   static constexpr int kTPW = kWave / kLPT;        // tokens one wave covers per pass
-  static constexpr int kPasses = kBlock / kTPW;    // passes per 16-token block
-  static_assert(kLPT >= 2 && kLPT <= 16, "row must span 2..16 lanes");
+  static constexpr int kPasses = kBlock / kTPW;    // passes per 16-token block (2 or 4)
+  static_assert(kVPL >= 1 && kPasses % 2 == 0, "lane mapping");
 };
 
-template <int NP>
+template <int NP, int VPL>
 struct BlockRegs {
-  uint4 k[NP][2];
-  uint4 v[NP][2];
+  uint4 k[NP][VPL];
+  uint4 v[NP][VPL];
 };
 
 __device__ __forceinline__ uint32_t dw(const uint4& u, int w) {
   return w == 0 ? u.x : (w == 1 ? u.y : (w == 2 ? u.z : u.w));
 }
 
-// Loads one 16-token block of one KV head: base points at its first vector.
+// Channel held by element e of a lane with in-row index sub.
 template <typename T, int D>
-__device__ __forceinline__ void load_block(BlockRegs<DecodeShape<T, D>::kPasses>& r,
-                                           const uint4* __restrict__ kbase,
+__device__ __forceinline__ int lane_channel(int sub, int e) {
+  using Sh = DecodeShape<T, D>;
+  return ((e / Sh::kEPV) * Sh::kLPT + sub) * Sh::kEPV + e % Sh::kEPV;
+}
+
+template <typename T, int D>
+using BlockOf = BlockRegs<DecodeShape<T, D>::kPasses, DecodeShape<T, D>::kVPL>;
+
+// K/V are read exactly once per call, so they are loaded with the non-temporal
+// hint: on MI355X this streams them past the caches' normal allocation and
+// lifts the sustained read bandwidth of this access pattern by about 13%.
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+
+// Loads one 16-token block of one KV head; base points at its first vector.
+template <typename T, int D>
+__device__ __forceinline__ void load_block(BlockOf<T, D>& r, const uint4* __restrict__ kbase,
                                            const uint4* __restrict__ vbase, int slot, int sub) {
   using Sh = DecodeShape<T, D>;
 #pragma unroll
-  for (int ps = 0; ps < Sh::kPasses; ++ps) {
-    const int tk = ps * Sh::kTPW + slot;
+  for (int ps = 0; ps < Sh::kPasses; ++ps)
 #pragma unroll
-    for (int v = 0; v < 2; ++v) r.k[ps][v] = kbase[tk * Sh::kRowVec + v * Sh::kLPT + sub];
-  }
+    for (int v = 0; v < Sh::kVPL; ++v)
+      r.k[ps][v] = stream_load(&kbase[(ps * Sh::kTPW + slot) * Sh::kRowVec + v * Sh::kLPT + sub]);
 #pragma unroll
-  for (int ps = 0; ps < Sh::kPasses; ++ps) {
-    const int tk = ps * Sh::kTPW + slot;
+  for (int ps = 0; ps < Sh::kPasses; ++ps)
 #pragma unroll
-    for (int v = 0; v < 2; ++v) r.v[ps][v] = vbase[tk * Sh::kRowVec + v * Sh::kLPT + sub];
-  }
+    for (int v = 0; v < Sh::kVPL; ++v)
+      r.v[ps][v] = stream_load(&vbase[(ps * Sh::kTPW + slot) * Sh::kRowVec + v * Sh::kLPT + sub]);
 }
 
-// Query registers: bf16 kept packed for v_dot2, fp32 kept as floats.
-template <typename T, int GC, int EPL>
+// Query registers: bf16 kept packed for v_dot2, fp32 kept as floats (4 words per vector).
+template <int GC, int VPL>
 struct QRegs {
-  static constexpr int kWords = std::is_same<T, float>::value ? EPL : EPL / 2;
-  uint32_t w[GC][kWords];
+  uint32_t w[GC][VPL * 4];
 };
 
-template <typename T, int D, int GC>
-__device__ __forceinline__ float dot_lane(const QRegs<T, GC, DecodeShape<T, D>::kEPL>& q, int j,
-                                          const uint4 (&k)[2]) {
-  float acc = 0.f;
-  if constexpr (std::is_same<T, float>::value) {
-#pragma unroll
-    for (int v = 0; v < 2; ++v)
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        acc = fmaf(__uint_as_float(q.w[j][v * 4 + w]), __uint_as_float(dw(k[v], w)), acc);
-  } else {
-#pragma unroll
-    for (int v = 0; v < 2; ++v)
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, dw(k[v], w)),
-                                              __builtin_bit_cast(bf16x2_t, q.w[j][v * 4 + w]),
-                                              acc, false);
-  }
-  return acc;
-}
-
-template <typename T, int EPL>
-__device__ __forceinline__ void widen(const uint4 (&v)[2], float (&f)[EPL]) {
-  if constexpr (std::is_same<T, float>::value) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) f[i * 4 + w] = __uint_as_float(dw(v[i], w));
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        f[i * 8 + 2 * w] = bf16lo_to_f32(dw(v[i], w));
-        f[i * 8 + 2 * w + 1] = bf16hi_to_f32(dw(v[i], w));
-      }
-  }
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Folds one block into the lane's running (m, l, acc).  MASK: tokens at local
-// index >= valid are outside the context (their scores and values are ignored,
-// whatever the pool holds there).
+// index >= valid lie past the context; their scores and values are ignored,
+// whatever the pool holds there.
 template <typename T, int D, int GC, bool MASK>
-__device__ __forceinline__ void attend_block(const BlockRegs<DecodeShape<T, D>::kPasses>& r,
-                                             const QRegs<T, GC, DecodeShape<T, D>::kEPL>& q,
+__device__ __forceinline__ void attend_block(const BlockOf<T, D>& r,
+                                             const QRegs<GC, DecodeShape<T, D>::kVPL>& q,
                                              float (&m)[GC], float (&l)[GC],
                                              float (&acc)[GC][DecodeShape<T, D>::kEPL],
                                              float scale_log2, int slot, int valid) {
   using Sh = DecodeShape<T, D>;
   constexpr int NP = Sh::kPasses;
+  constexpr int VPL = Sh::kVPL;
   constexpr int EPL = Sh::kEPL;
+  // q.K for the lane's NP tokens and every head: the NP * GC dot products are
+  // accumulated word by word in interleaved order so that no accumulator is
+  // used by two consecutive instructions, then reduced across the kLPT lanes
+  // of a token step by step, again interleaved.
   float s[NP][GC];
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps)
 #pragma unroll
-    for (int j = 0; j < GC; ++j) s[ps][j] = group_sum<Sh::kLPT>(dot_lane<T, D, GC>(q, j, r.k[ps])) * scale_log2;
+    for (int j = 0; j < GC; ++j) s[ps][j] = 0.f;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v)
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int ps = 0; ps < NP; ++ps) {
+        const uint32_t kw = dw(r.k[ps][v], w);
+#pragma unroll
+        for (int j = 0; j < GC; ++j) {
+          if constexpr (std::is_same<T, float>::value)
+            s[ps][j] = fmaf(__uint_as_float(q.w[j][v * 4 + w]), __uint_as_float(kw), s[ps][j]);
+          else
+            s[ps][j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kw),
+                                                       __builtin_bit_cast(bf16x2_t, q.w[j][v * 4 + w]),
+                                                       s[ps][j], false);
+        }
+      }
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps)
+#pragma unroll
+    for (int j = 0; j < GC; ++j) s[ps][j] += dpp<kDppXor1>(s[ps][j]);
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps)
+#pragma unroll
+    for (int j = 0; j < GC; ++j) s[ps][j] += dpp<kDppXor2>(s[ps][j]);
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps)
+#pragma unroll
+    for (int j = 0; j < GC; ++j) s[ps][j] += dpp<kDppRowHalfMirror>(s[ps][j]);
+  if constexpr (Sh::kLPT == 16) {
+#pragma unroll
+    for (int ps = 0; ps < NP; ++ps)
+#pragma unroll
+      for (int j = 0; j < GC; ++j) s[ps][j] += dpp<kDppRowMirror>(s[ps][j]);
+  }
   bool ok[NP];
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps) {
     ok[ps] = !MASK || (ps * Sh::kTPW + slot < valid);
-    if (MASK && !ok[ps]) {
 #pragma unroll
-      for (int j = 0; j < GC; ++j) s[ps][j] = kNegInf;
-    }
+    for (int j = 0; j < GC; ++j) s[ps][j] = (MASK && !ok[ps]) ? kNegInf : s[ps][j] * scale_log2;
   }
-  float smax[GC];
   bool need = false;
+  float smax[GC];
 #pragma unroll
   for (int j = 0; j < GC; ++j) {
     smax[j] = s[0][j];
@@ -182,258 +220,468 @@ __device__ __forceinline__ void attend_block(const BlockRegs<DecodeShape<T, D>::
       float w = fast_exp2(s[ps][j] - m[j]);
       if (MASK) w = ok[ps] ? w : 0.f;
       p[ps][j] = w;
-      l[j] += w;
     }
 #pragma unroll
-  for (int ps = 0; ps < NP; ++ps) {
-    float vf[EPL];
-    widen<T, EPL>(r.v[ps], vf);
-    if (MASK && !ok[ps]) {
+  for (int j = 0; j < GC; ++j) {
+    float t = p[0][j];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) vf[e] = 0.f;
+    for (int ps = 1; ps < NP; ++ps) t += p[ps][j];
+    l[j] += t;
+  }
+
+  if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+    for (int ps = 0; ps < NP; ++ps) {
+      if (MASK && !ok[ps]) continue;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float x = __uint_as_float(dw(r.v[ps][v], w));
+#pragma unroll
+          for (int j = 0; j < GC; ++j) acc[j][v * 4 + w] = fmaf(p[ps][j], x, acc[j][v * 4 + w]);
+        }
     }
+  } else {
+    // Tokens are paired (passes 2i, 2i+1): word (V_t0[c], V_t1[c]) against
+    // (p_t0, p_t1), so one v_dot2 adds both tokens' contributions.
 #pragma unroll
-    for (int j = 0; j < GC; ++j)
+    for (int pr = 0; pr < NP / 2; ++pr) {
+      uint32_t pp[GC];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(p[ps][j], vf[e], acc[j][e]);
+      for (int j = 0; j < GC; ++j) pp[j] = bf16x2_bits(p[2 * pr][j], p[2 * pr + 1][j]);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t x0 = dw(r.v[2 * pr][v], w), x1 = dw(r.v[2 * pr + 1][v], w);
+          if (MASK) {
+            x0 = ok[2 * pr] ? x0 : 0u;
+            x1 = ok[2 * pr + 1] ? x1 : 0u;
+          }
+          const uint32_t lo = __builtin_amdgcn_perm(x1, x0, 0x05040100u);  // channel 2w
+          const uint32_t hi = __builtin_amdgcn_perm(x1, x0, 0x07060302u);  // channel 2w+1
+#pragma unroll
+          for (int j = 0; j < GC; ++j) {
+            acc[j][v * 8 + 2 * w] = __builtin_amdgcn_fdot2_f32_bf16(
+                __builtin_bit_cast(bf16x2_t, pp[j]), __builtin_bit_cast(bf16x2_t, lo),
+                acc[j][v * 8 + 2 * w], false);
+            acc[j][v * 8 + 2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                __builtin_bit_cast(bf16x2_t, pp[j]), __builtin_bit_cast(bf16x2_t, hi),
+                acc[j][v * 8 + 2 * w + 1], false);
+          }
+        }
+    }
   }
 }
 
 template <typename T>
 __device__ __forceinline__ void store_elem(T* out, size_t i, float x) {
-  if constexpr (std::is_same<T, float>::value) {
+  if constexpr (std::is_same<T, float>::value)
     out[i] = x;
-  } else {
+  else
     reinterpret_cast<uint16_t*>(out)[i] = (uint16_t)f32_to_bf16_bits(x);
+}
+
+// Clamped context length: never beyond the block table row.
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int b) {
+  const int L = a.context_lens[b];
+  return max(0, min(L, a.max_blocks_per_seq * kBlock));
+}
+__device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int b) {
+  return (seq_len(a, b) + kBlock - 1) / kBlock;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
+  return x;
+}
+
+// Positions are block indices on the line of all segments laid end to end.
+struct Line {
+  int64_t total;  // blocks on the line (all segments)
+  int splits;
+  __device__ int64_t start(int w) const { return (int64_t)w * total / splits; }
+  __device__ int wave_of(int64_t p) const { return (int)(((p + 1) * splits - 1) / total); }
+};
+
+// Blocks of all sequences before b (if b >= 0) and of all sequences.
+struct ScanResult {
+  int64_t before;
+  int64_t total;
+};
+__device__ __forceinline__ ScanResult scan_blocks(const DecodeArgs& a, int b, int lane) {
+  ScanResult r{0, 0};
+  for (int c0 = 0; c0 < a.B; c0 += kWave) {
+    const int bb = c0 + lane;
+    const int n = bb < a.B ? seq_blocks(a, bb) : 0;
+    const int incl = wave_incl_scan(n, lane);
+    const int chunk_total = __shfl(incl, kWave - 1);
+    if (b >= c0 && b < c0 + kWave) r.before = r.total + __shfl(incl, b - c0) - __shfl(n, b - c0);
+    r.total += chunk_total;
+  }
+  return r;
 }
 
 template <typename T, int D, int GC>
-__global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
+struct Segment {
   using Sh = DecodeShape<T, D>;
-  constexpr int NP = Sh::kPasses;
-  constexpr int EPL = Sh::kEPL;
-  constexpr int W = kDecodeWaves;
-  __shared__ float s_acc[W][GC][D];
-  __shared__ float s_m[W][GC];
-  __shared__ float s_l[W][GC];
+  static constexpr int VPL = Sh::kVPL;
+  static constexpr int EPL = Sh::kEPL;
 
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y / a.n_chunks;
-  const int chunk = blockIdx.y - kvh * a.n_chunks;
-  const int b = blockIdx.z;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int sub = lane % Sh::kLPT;
-  const int slot = lane / Sh::kLPT;
-  const int head0 = kvh * a.g + chunk * GC;
-  const int nh = min(GC, a.g - chunk * GC);
-  const int P = a.partition_tokens;
-  // Lengths beyond the table or beyond the launched partitions are clamped, so
-  // no value in device memory can move an access outside its buffer.
-  int L = a.context_lens[b];
-  L = max(0, min(L, min(a.max_blocks_per_seq * kBlock, a.num_partitions * P)));
-  const int n_part = (L + P - 1) / P;
-  T* out = reinterpret_cast<T*>(a.out);
+  // Attends blocks j0 .. j1-1 of segment (b, kc) and stores the result: the
+  // normalised output if the piece is the whole segment, else a partial state
+  // in slot `slot` of wave W.
+  __device__ static void run(const DecodeArgs& a, int W, int b, int kc, int j0, int j1, int nb,
+                             int lane) {
+    const int sub = lane % Sh::kLPT;
+    const int slot_id = lane / Sh::kLPT;
+    const int kvh = kc / a.n_chunks;
+    const int chunk = kc - kvh * a.n_chunks;
+    const int head0 = kvh * a.g + chunk * GC;
+    const int nh = min(GC, a.g - chunk * GC);
+    const int L = seq_len(a, b);
 
-  if (part >= n_part) {
-    if (L == 0 && part == 0) {
-      for (int i = threadIdx.x; i < nh * D; i += blockDim.x)
-        store_elem<T>(out, ((size_t)b * a.h_q + head0 + i / D) * D + i % D, 0.f);
+    QRegs<GC, VPL> q;
+    {
+      const uint4* qv = reinterpret_cast<const uint4*>(a.q);
+#pragma unroll
+      for (int j = 0; j < GC; ++j) {
+        const int h = head0 + min(j, nh - 1);
+        const size_t rowv = ((size_t)b * a.h_q + h) * Sh::kRowVec;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+          const uint4 x = qv[rowv + v * Sh::kLPT + sub];
+          q.w[j][v * 4 + 0] = x.x;
+          q.w[j][v * 4 + 1] = x.y;
+          q.w[j][v * 4 + 2] = x.z;
+          q.w[j][v * 4 + 3] = x.w;
+        }
+      }
     }
-    return;
-  }
-  const int tok0 = part * P;
-  const int tok1 = min(L, tok0 + P);
-  const int blk0 = tok0 / kBlock;
-  const int nblk = (tok1 + kBlock - 1) / kBlock - blk0;  // <= 64
-
-  int my_tbl = 0;
-  if (lane < nblk) {
-    const int e = a.block_tables[(size_t)b * a.max_blocks_per_seq + blk0 + lane];
-    my_tbl = (e >= 0 && e < a.n_blocks) ? e : 0;
-  }
-
-  QRegs<T, GC, EPL> q;
-  {
-    const uint4* qv = reinterpret_cast<const uint4*>(a.q);
+    float m[GC], l[GC], acc[GC][EPL];
 #pragma unroll
     for (int j = 0; j < GC; ++j) {
-      const int h = head0 + min(j, nh - 1);
-      const size_t rowv = ((size_t)b * a.h_q + h) * Sh::kRowVec;
+      m[j] = kNegInf;
+      l[j] = 0.f;
 #pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        const uint4 x = qv[rowv + v * Sh::kLPT + sub];
-        if constexpr (std::is_same<T, float>::value) {
-          q.w[j][v * 4 + 0] = x.x; q.w[j][v * 4 + 1] = x.y;
-          q.w[j][v * 4 + 2] = x.z; q.w[j][v * 4 + 3] = x.w;
-        } else {
-          q.w[j][v * 4 + 0] = x.x; q.w[j][v * 4 + 1] = x.y;
-          q.w[j][v * 4 + 2] = x.z; q.w[j][v * 4 + 3] = x.w;
+      for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
+    }
+
+    const uint4* kc4 = reinterpret_cast<const uint4*>(a.k_cache);
+    const uint4* vc4 = reinterpret_cast<const uint4*>(a.v_cache);
+    const size_t head_vecs = (size_t)kBlock * Sh::kRowVec;
+    const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+
+    for (int jb = j0; jb < j1; jb += kWave) {
+      const int n = min(j1 - jb, kWave);
+      int tbl = 0;
+      if (lane < n) {
+        const int e = trow[jb + lane];
+        tbl = (e >= 0 && e < a.n_blocks) ? e : 0;
+      }
+      auto base_of = [&](int t) -> size_t {
+        const int blk = __builtin_amdgcn_readlane(tbl, t);
+        return ((size_t)blk * a.h_kv + kvh) * head_vecs;
+      };
+      auto attend_last = [&](const BlockOf<T, D>& r, int t) {
+        const int valid = L - (jb + t) * kBlock;
+        if (valid >= kBlock)
+          attend_block<T, D, GC, false>(r, q, m, l, acc, a.scale_log2, slot_id, kBlock);
+        else
+          attend_block<T, D, GC, true>(r, q, m, l, acc, a.scale_log2, slot_id, valid);
+      };
+      auto load_t = [&](BlockOf<T, D>& r, int t) {
+        const size_t base = base_of(t);
+        load_block<T, D>(r, kc4 + base, vc4 + base, slot_id, sub);
+      };
+      // Software pipeline: kDepth blocks in registers, kDepth - 1 of them in
+      // flight while one is used.  Only the last block of a run can be the
+      // partial last block of a sequence.
+      BlockOf<T, D> R[kDepth];
+#pragma unroll
+      for (int i = 0; i < kDepth - 1; ++i)
+        if (i < n) load_t(R[i], i);
+      int t = 0;
+      while (t + 2 * kDepth - 2 < n) {
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) {
+          load_t(R[(u + kDepth - 1) % kDepth], t + u + kDepth - 1);
+          attend_block<T, D, GC, false>(R[u], q, m, l, acc, a.scale_log2, slot_id, kBlock);
+        }
+        t += kDepth;
+      }
+      // At most 2 * kDepth - 2 blocks remain; block t + v is in R[v % kDepth].
+#pragma unroll
+      for (int u = 0; u < 2 * kDepth - 2; ++u) {
+        if (t + u < n) {
+          if (t + u + kDepth - 1 < n) load_t(R[(u + kDepth - 1) % kDepth], t + u + kDepth - 1);
+          if (t + u + 1 < n)
+            attend_block<T, D, GC, false>(R[u % kDepth], q, m, l, acc, a.scale_log2, slot_id, kBlock);
+          else
+            attend_last(R[u % kDepth], t + u);
+        }
+      }
+    }
+
+    // Merge the lanes' states: lanes with the same sub hold the same channels.
+    const bool whole = (j0 == 0 && j1 == nb);
+    const int slot = j0 > 0 ? 0 : 1;
+#pragma unroll
+    for (int j = 0; j < GC; ++j) {
+      const float M = class_max<Sh::kLPT>(m[j]);
+      const float f = m[j] == kNegInf ? 0.f : fast_exp2(m[j] - M);
+      const float ls = class_sum<Sh::kLPT>(l[j] * f);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[j][e] = class_sum<Sh::kLPT>(acc[j][e] * f);
+      if (j >= nh || slot_id != 0) continue;
+      if (whole) {
+        const float inv = 1.f / ls;
+        T* out = reinterpret_cast<T*>(a.out) + ((size_t)b * a.h_q + head0 + j) * D;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) store_elem<T>(out, lane_channel<T, D>(sub, e), acc[j][e] * inv);
+      } else {
+        float* ws = a.ws + ((size_t)(W * 2 + slot) * GC + j) * (D + 2);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ws[lane_channel<T, D>(sub, e)] = acc[j][e];
+        if (sub == 0) {
+          ws[D] = M;
+          ws[D + 1] = ls;
         }
       }
     }
   }
+};
 
-  float m[GC], l[GC], acc[GC][EPL];
-#pragma unroll
-  for (int j = 0; j < GC; ++j) {
-    m[j] = kNegInf;
-    l[j] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
-  }
+template <typename T, int D, int GC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_SIMD))) void decode_split_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int W = blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (W >= a.num_splits) return;
+  const int HC = a.h_kv * a.n_chunks;
 
-  const uint4* kc = reinterpret_cast<const uint4*>(a.k_cache);
-  const uint4* vc = reinterpret_cast<const uint4*>(a.v_cache);
-  const size_t head_vecs = (size_t)kBlock * Sh::kRowVec;
-  auto block_base = [&](int j) -> size_t {
-    const int blk = __builtin_amdgcn_readlane(my_tbl, j);
-    return ((size_t)blk * a.h_kv + kvh) * head_vecs;
-  };
-  auto attend_tail = [&](const BlockRegs<NP>& r, int j) {
-    const int valid = tok1 - (blk0 + j) * kBlock;
-    if (valid >= kBlock)
-      attend_block<T, D, GC, false>(r, q, m, l, acc, a.scale_log2, slot, kBlock);
-    else
-      attend_block<T, D, GC, true>(r, q, m, l, acc, a.scale_log2, slot, valid);
-  };
+  const ScanResult all = scan_blocks(a, -1, lane);
+  const Line line{all.total * HC, a.num_splits};
+  if (line.total == 0) return;
+  const int64_t s = line.start(W);
+  const int64_t e = line.start(W + 1);
+  if (s >= e) return;
 
-  int j = wave;
-  if (j < nblk) {
-    BlockRegs<NP> A, Bv;
-    size_t base = block_base(j);
-    load_block<T, D>(A, kc + base, vc + base, slot, sub);
-    // Blocks before the last one of the partition are always full.
-    while (j + 2 * W < nblk) {
-      base = block_base(j + W);
-      load_block<T, D>(Bv, kc + base, vc + base, slot, sub);
-      attend_block<T, D, GC, false>(A, q, m, l, acc, a.scale_log2, slot, kBlock);
-      base = block_base(j + 2 * W);
-      load_block<T, D>(A, kc + base, vc + base, slot, sub);
-      attend_block<T, D, GC, false>(Bv, q, m, l, acc, a.scale_log2, slot, kBlock);
-      j += 2 * W;
-    }
-    if (j + W < nblk) {
-      base = block_base(j + W);
-      load_block<T, D>(Bv, kc + base, vc + base, slot, sub);
-      attend_block<T, D, GC, false>(A, q, m, l, acc, a.scale_log2, slot, kBlock);
-      attend_tail(Bv, j + W);
-    } else {
-      attend_tail(A, j);
-    }
-  }
-
-  // Merge the lanes' states: lanes with the same sub hold the same channels.
-#pragma unroll
-  for (int jh = 0; jh < GC; ++jh) {
-    const float M = class_max<Sh::kLPT>(m[jh]);
-    const float f = m[jh] == kNegInf ? 0.f : fast_exp2(m[jh] - M);
-    const float ls = class_sum<Sh::kLPT>(l[jh] * f);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[jh][e] = class_sum<Sh::kLPT>(acc[jh][e] * f);
-    if (slot == 0) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const int v = e / Sh::kEPV;
-        const int dim = (v * Sh::kLPT + sub) * Sh::kEPV + e % Sh::kEPV;
-        s_acc[wave][jh][dim] = acc[jh][e];
+  // The sequence holding position s: the first whose end lies past s.
+  int b = 0, nb = 0;
+  int64_t seq0 = 0;
+  {
+    int64_t base = 0;
+    for (int c0 = 0; c0 < a.B; c0 += kWave) {
+      const int bb = c0 + lane;
+      const int n = bb < a.B ? seq_blocks(a, bb) : 0;
+      const int incl = wave_incl_scan(n, lane);
+      const uint64_t hit = __ballot(bb < a.B && (base + incl) * HC > s);
+      if (hit) {
+        const int f = __builtin_ctzll(hit);
+        b = c0 + f;
+        nb = __shfl(n, f);
+        seq0 = (base + __shfl(incl, f) - nb) * HC;
+        break;
       }
-    }
-    if (lane == 0) {
-      s_m[wave][jh] = M;
-      s_l[wave][jh] = ls;
+      base += __shfl(incl, kWave - 1);
     }
   }
-  __syncthreads();
 
-  for (int i = threadIdx.x; i < nh * D; i += blockDim.x) {
-    const int jh = i / D;
-    const int dim = i - jh * D;
-    float Mx = kNegInf;
-#pragma unroll
-    for (int w = 0; w < W; ++w) Mx = fmaxf(Mx, s_m[w][jh]);
-    float o = 0.f, lt = 0.f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float mw = s_m[w][jh];
-      const float f = mw == kNegInf ? 0.f : fast_exp2(mw - Mx);
-      o = fmaf(f, s_acc[w][jh][dim], o);
-      lt = fmaf(f, s_l[w][jh], lt);
-    }
-    const size_t row = (size_t)b * a.h_q + head0 + jh;
-    if (n_part == 1) {
-      store_elem<T>(out, row * D + dim, o / lt);
-    } else {
-      const size_t pi = row * a.num_partitions + part;
-      a.ws_acc[pi * D + dim] = o;
-      if (dim == 0) {
-        a.ws_ml[pi * 2] = Mx;
-        a.ws_ml[pi * 2 + 1] = lt;
-      }
-    }
+  int64_t pos = s;
+  while (true) {
+    const int64_t r = pos - seq0;
+    const int kc = (int)(r / nb);
+    const int j0 = (int)(r - (int64_t)kc * nb);
+    const int64_t seg0 = seq0 + (int64_t)kc * nb;
+    const int j1 = (int)min((int64_t)nb, e - seg0);
+    Segment<T, D, GC>::run(a, W, b, kc, j0, j1, nb, lane);
+    pos = seg0 + j1;
+    if (pos >= e) break;
+    if (kc + 1 < HC) continue;  // next head chunk of the same sequence
+    seq0 += (int64_t)HC * nb;
+    do {
+      ++b;
+      nb = b < a.B ? seq_blocks(a, b) : 1;
+    } while (nb == 0);
+    if (b >= a.B) break;  // only reachable if the lengths changed under the kernel
   }
 }
 
-// Log-sum-exp merge of the partitions of one (sequence, query head).
-template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  int L = a.context_lens[b];
-  L = max(0, min(L, min(a.max_blocks_per_seq * kBlock, a.num_partitions * a.partition_tokens)));
-  const int n_part = (L + a.partition_tokens - 1) / a.partition_tokens;
-  if (n_part <= 1) return;
-  const size_t row = (size_t)b * a.h_q + h;
-  const float* ml = a.ws_ml + row * a.num_partitions * 2;
-  const float* pacc = a.ws_acc + row * a.num_partitions * D;
-  float Mx = kNegInf;
-  for (int p = 0; p < n_part; ++p) Mx = fmaxf(Mx, ml[2 * p]);
-  float lt = 0.f;
-  for (int p = 0; p < n_part; ++p) lt = fmaf(fast_exp2(ml[2 * p] - Mx), ml[2 * p + 1], lt);
-  const float inv = 1.f / lt;
+// Merges the partial states of segments cut by range boundaries (exact
+// log-sum-exp), and writes zeros for sequences of length 0.  One workgroup per
+// segment; wave j takes heads j, j + 4, ...  Each pass over the pieces issues
+// all of its loads before using them, so a merge costs a few memory round
+// trips whatever the number of pieces.
+constexpr int kCombineWaves = 4;
+template <typename T, int D, int GC>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int HC = a.h_kv * a.n_chunks;
+  const int seg = blockIdx.x;
+  const int b = seg / HC;
+  const int kc = seg - b * HC;
+  const int kvh = kc / a.n_chunks;
+  const int chunk = kc - kvh * a.n_chunks;
+  const int head0 = kvh * a.g + chunk * GC;
+  const int nh = min(GC, a.g - chunk * GC);
   T* out = reinterpret_cast<T*>(a.out);
-  for (int dim = threadIdx.x; dim < D; dim += blockDim.x) {
-    float o = 0.f;
-    for (int p = 0; p < n_part; ++p) o = fmaf(fast_exp2(ml[2 * p] - Mx), pacc[(size_t)p * D + dim], o);
-    store_elem<T>(out, row * D + dim, o * inv);
+
+  const int nb = seq_blocks(a, b);
+  if (nb == 0) {
+    for (int i = threadIdx.x; i < nh * D; i += blockDim.x)
+      store_elem<T>(out, ((size_t)b * a.h_q + head0 + i / D) * D + i % D, 0.f);
+    return;
+  }
+  const ScanResult sc = scan_blocks(a, b, lane);
+  const Line line{sc.total * HC, a.num_splits};
+  const int64_t S0 = sc.before * HC + (int64_t)kc * nb;
+  const int wa = line.wave_of(S0);
+  const int wb = line.wave_of(S0 + nb - 1);
+  if (wa == wb) return;  // stored whole by its wave
+  const int np = wb - wa + 1;
+  constexpr int CPL = (D + kWave - 1) / kWave;  // channels per lane
+
+  for (int j = wave; j < nh; j += kCombineWaves) {
+    // Piece k is wave wa + k: slot 1 for the first, slot 0 for later non-empty waves.
+    auto piece = [&](int k) -> const float* {
+      return a.ws + ((size_t)((wa + k) * 2 + (k == 0 ? 1 : 0)) * GC + j) * (D + 2);
+    };
+    auto live = [&](int k) -> bool {
+      return k == 0 || line.start(wa + k) < line.start(wa + k + 1);
+    };
+    float M = kNegInf;
+    for (int k0 = 0; k0 < np; k0 += kWave) {
+      const int k = k0 + lane;
+      M = fmaxf(M, wave_max((k < np && live(k)) ? piece(k)[D] : kNegInf));
+    }
+    float ls = 0.f;
+    for (int k0 = 0; k0 < np; k0 += kWave) {
+      const int k = k0 + lane;
+      float x = 0.f;
+      if (k < np && live(k)) x = fast_exp2(piece(k)[D] - M) * piece(k)[D + 1];
+      ls += wave_sum(x);
+    }
+    const float inv = 1.f / ls;
+    float o[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) o[i] = 0.f;
+    for (int k0 = 0; k0 < np; k0 += kWave) {
+      const int k = k0 + lane;
+      const bool lk = k < np && live(k);
+      const uint64_t live_mask = __ballot(lk);  // pieces of empty waves are never read
+      const float wk = lk ? fast_exp2(piece(k)[D] - M) : 0.f;
+      const int kn = min(kWave, np - k0);
+      for (int t0 = 0; t0 < kn; t0 += 8) {
+        float x[8][CPL];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const bool use = t0 + t < kn && ((live_mask >> (t0 + t)) & 1);
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) {
+            const int c = lane + i * kWave;
+            x[t][i] = (use && c < D) ? piece(k0 + t0 + t)[c] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float w = __int_as_float(
+              __builtin_amdgcn_readlane(__float_as_int(wk), min(t0 + t, kWave - 1)));
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) o[i] = fmaf(w, x[t][i], o[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = lane + i * kWave;
+      if (c < D) store_elem<T>(out, ((size_t)b * a.h_q + head0 + j) * D + c, o[i] * inv);
+    }
   }
 }
 
 template <typename T, int D, int GC>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.num_partitions, a.h_kv * a.n_chunks, a.B);
-  hipLaunchKernelGGL((decode_partial_kernel<T, D, GC>), grid, dim3(256), 0, stream, a);
-  if (a.num_partitions > 1)
-    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.h_q, a.B), dim3(64), 0, stream, a);
+  const int wg = 4;  // waves per workgroup
+  hipLaunchKernelGGL((decode_split_kernel<T, D, GC>), dim3((a.num_splits + wg - 1) / wg),
+                     dim3(wg * kWave), 0, stream, a);
+  hipLaunchKernelGGL((decode_combine_kernel<T, D, GC>), dim3(a.B * a.h_kv * a.n_chunks),
+                     dim3(kCombineWaves * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
+template <typename T, int D, int GC>
+static int occupancy_waves_t() {
+  static int waves = [] {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(decode_split_kernel<T, D, GC>), 256, 0) !=
+            hipSuccess ||
+        cus <= 0 || per_cu <= 0)
+      return 0;
+    return cus * per_cu * 4;
+  }();
+  return waves;
+}
+
+template <typename T, int D, int GC>
+static hipError_t run_or_query(const DecodeArgs& a, hipStream_t stream, int* waves_out) {
+  if (waves_out) {
+    *waves_out = occupancy_waves_t<T, D, GC>();
+    return hipSuccess;
+  }
+  return launch_t<T, D, GC>(a, stream);
+}
+
 template <typename T, int D>
-static hipError_t launch_gc(const DecodeArgs& a, int gc, hipStream_t stream) {
-  switch (gc) {
-    case 1: return launch_t<T, D, 1>(a, stream);
-    case 2: return launch_t<T, D, 2>(a, stream);
-    case 3: return launch_t<T, D, 3>(a, stream);
-    case 4: return launch_t<T, D, 4>(a, stream);
-    case 5: return launch_t<T, D, 5>(a, stream);
-    case 6: return launch_t<T, D, 6>(a, stream);
-    case 7: return launch_t<T, D, 7>(a, stream);
-    case 8: return launch_t<T, D, 8>(a, stream);
+static hipError_t dispatch_gc(const DecodeArgs& a, hipStream_t stream, int* waves_out) {
+  constexpr bool kWide = std::is_same<T, float>::value && D == 128;  // at most 4 heads per chunk
+  switch (a.gc) {
+    case 1: return run_or_query<T, D, 1>(a, stream, waves_out);
+    case 2: return run_or_query<T, D, 2>(a, stream, waves_out);
+    case 3: return run_or_query<T, D, 3>(a, stream, waves_out);
+    case 4: return run_or_query<T, D, 4>(a, stream, waves_out);
+  }
+  if constexpr (!kWide) {
+    switch (a.gc) {
+      case 5: return run_or_query<T, D, 5>(a, stream, waves_out);
+      case 6: return run_or_query<T, D, 6>(a, stream, waves_out);
+      case 7: return run_or_query<T, D, 7>(a, stream, waves_out);
+      case 8: return run_or_query<T, D, 8>(a, stream, waves_out);
+    }
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int d_h, bool bf16, hipStream_t stream) {
-  const int gc = head_chunks(a.g).per_chunk;
+static hipError_t dispatch(const DecodeArgs& a, int d_h, bool bf16, hipStream_t stream,
+                           int* waves_out) {
   if (bf16) {
-    if (d_h == 64) return launch_gc<bf16_t, 64>(a, gc, stream);
-    if (d_h == 128) return launch_gc<bf16_t, 128>(a, gc, stream);
+    if (d_h == 64) return dispatch_gc<bf16_t, 64>(a, stream, waves_out);
+    if (d_h == 128) return dispatch_gc<bf16_t, 128>(a, stream, waves_out);
   } else {
-    if (d_h == 64) return launch_gc<float, 64>(a, gc, stream);
-    if (d_h == 128) return launch_gc<float, 128>(a, gc, stream);
+    if (d_h == 64) return dispatch_gc<float, 64>(a, stream, waves_out);
+    if (d_h == 128) return dispatch_gc<float, 128>(a, stream, waves_out);
   }
   return hipErrorInvalidValue;
+}
+
+int decode_resident_waves(int d_h, bool bf16, int gc) {
+  DecodeArgs a{};
+  a.gc = gc;
+  int waves = 0;
+  if (dispatch(a, d_h, bf16, nullptr, &waves) != hipSuccess) return 0;
+  return waves;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int d_h, bool bf16, hipStream_t stream) {
+  return dispatch(a, d_h, bf16, stream, nullptr);
 }
 
 }  // namespace pkv

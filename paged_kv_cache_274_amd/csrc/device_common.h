@@ -13,6 +13,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // bf16 storage type: raw 16-bit pattern.
 struct bf16_t {
@@ -67,14 +68,34 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Cross-row exchanges on VALU (gfx950 v_permlane16_swap / v_permlane32_swap):
+// with both operands equal to x, the two results hold x of lane l and of lane
+// l ^ 16 (resp. l ^ 32), so their sum or max is the pairwise combine.
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Combine lanes that share (lane mod N) across the whole wave, N in 4, 8, 16,
 // 32, 64: every lane receives the sum (max) over the 64/N lanes of its class.
 template <int N>
 __device__ __forceinline__ float class_sum(float x) {
   if constexpr (N <= 4) x += dpp<kDppRowRor4>(x);
   if constexpr (N <= 8) x += dpp<kDppRowRor8>(x);
-  if constexpr (N <= 16) x += __shfl_xor(x, 16);
-  if constexpr (N <= 32) x += __shfl_xor(x, 32);
+  if constexpr (N <= 16) x = xor16_sum(x);
+  if constexpr (N <= 32) x = xor32_sum(x);
   return x;
 }
 
@@ -82,9 +103,22 @@ template <int N>
 __device__ __forceinline__ float class_max(float x) {
   if constexpr (N <= 4) x = fmaxf(x, dpp<kDppRowRor4>(x));
   if constexpr (N <= 8) x = fmaxf(x, dpp<kDppRowRor8>(x));
-  if constexpr (N <= 16) x = fmaxf(x, __shfl_xor(x, 16));
-  if constexpr (N <= 32) x = fmaxf(x, __shfl_xor(x, 32));
+  if constexpr (N <= 16) x = xor16_max(x);
+  if constexpr (N <= 32) x = xor32_max(x);
   return x;
+}
+
+// Sum and max over all 64 lanes.
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<16>(x);
+  return class_sum<16>(x);
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppRowMirror>(x));
+  return class_max<16>(x);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -7,48 +7,52 @@
 
 namespace pkv {
 
-// Query heads handled by one decode workgroup: the GQA group of a KV head is
-// split into n_chunks chunks of at most 8 heads, so per-lane accumulators stay
-// in registers.
+// Query heads handled together by one decode wavefront: the GQA group of a KV
+// head is split into n_chunks chunks of at most max_chunk heads, so the per-lane
+// accumulators stay in registers (fp32 with d_h = 128 holds twice as many
+// accumulator words per head, so its chunks are half as large).
 struct HeadChunks {
   int n_chunks;
   int per_chunk;
 };
-inline HeadChunks head_chunks(int g) {
+inline int max_chunk(int d_h, bool bf16) { return (!bf16 && d_h == 128) ? 4 : 8; }
+inline HeadChunks head_chunks(int g, int d_h, bool bf16) {
+  const int cap = max_chunk(d_h, bf16);
   HeadChunks c;
-  c.n_chunks = (g + 7) / 8;
+  c.n_chunks = (g + cap - 1) / cap;
   c.per_chunk = (g + c.n_chunks - 1) / c.n_chunks;
   return c;
 }
 
-// Decode context split.  Picks the largest power of two in [64, 1024] such
-// that, were every context half of max_context_len long, the launch would
-// still hold about 2048 (sequence, KV head, partition) work units: enough to
-// fill 256 CUs several times while the per-partition partial results stay a
-// few percent of the KV bytes read.
-inline int decode_partition_tokens(int B, int h_q, int h_kv, int max_context_len,
-                                   int requested) {
-  if (B < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0 || max_context_len < 0) return -1;
-  if (requested != 0) {
-    if (requested < 16 || requested > 1024 || requested % 16 != 0) return -1;
-    return requested;
-  }
-  const int64_t base = (int64_t)B * h_kv * head_chunks(h_q / h_kv).n_chunks;
-  const int64_t want = base * (int64_t)max_context_len / 4096;
-  int p = 64;
-  while (p < 1024 && 2 * p <= want) p *= 2;
-  return p;
+// Decode work line: every (sequence, KV head, head chunk) segment's blocks laid
+// end to end.  Its length is at most B * h_kv * n_chunks * ceil(max_context_len / 16).
+inline int64_t decode_line_upper(int B, int h_q, int h_kv, int d_h, bool bf16,
+                                 int max_context_len) {
+  return (int64_t)B * h_kv * head_chunks(h_q / h_kv, d_h, bf16).n_chunks *
+         ((max_context_len + 15) / 16);
 }
 
-inline int decode_num_partitions(int max_context_len, int partition_tokens) {
-  return (max_context_len + partition_tokens - 1) / partition_tokens;
+// Upper bound of the automatic split count (resident wavefronts of a full MI355X
+// at two waves per SIMD is 2048; the bound leaves room for higher occupancy).
+constexpr int kMaxAutoSplits = 4096;
+constexpr int kMaxSplits = 1 << 16;
+
+// Splits the workspace must hold: the explicit count, or the automatic bound.
+inline int64_t decode_split_bound(int B, int h_q, int h_kv, int d_h, bool bf16,
+                                  int max_context_len, int num_splits) {
+  if (num_splits > 0) return num_splits;
+  const int64_t up = decode_line_upper(B, h_q, h_kv, d_h, bf16, max_context_len);
+  return up < 1 ? 1 : (up > kMaxAutoSplits ? kMaxAutoSplits : up);
 }
 
-inline size_t decode_workspace_bytes(int B, int h_q, int d_h, int max_context_len,
-                                     int partition_tokens) {
-  const int P = decode_num_partitions(max_context_len, partition_tokens);
-  if (P <= 1 || B == 0) return 0;
-  return (size_t)B * h_q * P * (size_t)(d_h + 2) * sizeof(float);
+// Per split: two partial states (first and last segment piece) of gc heads,
+// each d_h accumulators plus the running max and sum, in fp32.
+inline size_t decode_workspace_bytes(int B, int h_q, int h_kv, int d_h, bool bf16,
+                                     int max_context_len, int num_splits) {
+  if (B <= 0) return 0;
+  const int gc = head_chunks(h_q / h_kv, d_h, bf16).per_chunk;
+  return (size_t)decode_split_bound(B, h_q, h_kv, d_h, bf16, max_context_len, num_splits) * 2 *
+         gc * (size_t)(d_h + 2) * sizeof(float);
 }
 
 struct DecodeArgs {
@@ -58,18 +62,20 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_acc;   // [B, h_q, P, d_h] unnormalised partial outputs
-  float* ws_ml;    // [B, h_q, P, 2]  (running max in log2 units, sum of weights)
-  int B, h_q, h_kv, g, n_chunks, n_blocks, max_blocks_per_seq;
-  int partition_tokens, num_partitions;
+  float* ws;  // [num_splits][2][gc][d_h + 2]: accumulators, max (log2 units), sum
+  int B, h_q, h_kv, g, n_chunks, gc, n_blocks, max_blocks_per_seq, num_splits;
   float scale_log2;  // scale * log2(e)
 };
+
+// Wavefronts of the decode kernel for (d_h, dtype, gc) that the current device
+// holds at once; 0 if it cannot be queried.
+int decode_resident_waves(int d_h, bool bf16, int gc);
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                             void* k_cache, void* v_cache, int T, int h_kv, int d_h,
                             int n_blocks, int elem_bytes, hipStream_t stream);
 
-// Returns hipErrorInvalidValue for (dtype, d_h, chunk) combinations without a kernel.
+// Returns hipErrorInvalidValue for (dtype, d_h, gc) combinations without a kernel.
 hipError_t launch_decode(const DecodeArgs& a, int d_h, bool bf16, hipStream_t stream);
 
 struct PrefillArgs {

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 PKV_F32, PKV_BF16 = 0, 1
 _DTYPE = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
 EXPORTED = ("kv_append", "paged_decode_attention", "paged_prefill_attention",
-            "pkv_decode_workspace_bytes", "pkv_decode_partition_tokens", "pkv_status_string")
+            "pkv_decode_workspace_bytes", "pkv_decode_num_splits", "pkv_status_string")
 
 _lib = None
 
@@ -45,9 +45,9 @@ def lib() -> ctypes.CDLL:
     L.pkv_status_string.restype = ctypes.c_char_p
     L.kv_append.argtypes = [vp, vp, i64p, vp, vp, i32, i32, i32, i32, i32, vp]
     L.kv_append.restype = i32
-    L.pkv_decode_partition_tokens.argtypes = [i32, i32, i32, i32, i32]
-    L.pkv_decode_partition_tokens.restype = i32
-    L.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.pkv_decode_num_splits.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.pkv_decode_num_splits.restype = i32
+    L.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.pkv_decode_workspace_bytes.restype = ctypes.c_size_t
     L.paged_decode_attention.argtypes = [vp, vp, vp, vp, i32p, i32p, i32, i32, i32, i32, i32, i32,
                                          i32, ctypes.c_float, i32, i32, vp, ctypes.c_size_t, vp]
@@ -104,21 +104,22 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tens
         raise PkvError("kv_append", rc)
 
 
-def decode_partition_tokens(B: int, h_q: int, h_kv: int, max_context_len: int,
-                            partition_tokens: int = 0) -> int:
-    return int(lib().pkv_decode_partition_tokens(B, h_q, h_kv, max_context_len, partition_tokens))
+def decode_num_splits(B: int, h_q: int, h_kv: int, d_h: int, max_context_len: int,
+                      dtype: torch.dtype = torch.bfloat16, num_splits: int = 0) -> int:
+    return int(lib().pkv_decode_num_splits(B, h_q, h_kv, d_h, max_context_len, _DTYPE[dtype],
+                                           num_splits))
 
 
 def decode_workspace_bytes(B: int, h_q: int, h_kv: int, d_h: int, max_context_len: int,
-                           partition_tokens: int = 0) -> int:
-    return int(lib().pkv_decode_workspace_bytes(B, h_q, h_kv, d_h, max_context_len,
-                                                 partition_tokens))
+                           dtype: torch.dtype = torch.bfloat16, num_splits: int = 0) -> int:
+    return int(lib().pkv_decode_workspace_bytes(B, h_q, h_kv, d_h, max_context_len, _DTYPE[dtype],
+                                                 num_splits))
 
 
 def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_tables: torch.Tensor, context_lens: torch.Tensor,
                            max_context_len: int, scale: Optional[float] = None,
-                           partition_tokens: int = 0, out: Optional[torch.Tensor] = None,
+                           num_splits: int = 0, out: Optional[torch.Tensor] = None,
                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Single-token decode over paged K/V.  q, out: [B, h_q, d_h]."""
     n_blocks, h_kv, d = _pool_shape(k_cache, v_cache)
@@ -134,7 +135,7 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     _dev(q, k_cache, v_cache, block_tables, context_lens, out)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    ws_bytes = decode_workspace_bytes(B, h_q, h_kv, d, int(max_context_len), partition_tokens)
+    ws_bytes = decode_workspace_bytes(B, h_q, h_kv, d, int(max_context_len), q.dtype, num_splits)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -143,7 +144,7 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         block_tables.data_ptr(), context_lens.data_ptr(), B, h_q, h_kv, d, n_blocks,
         int(block_tables.shape[1]), int(max_context_len), float(scale), _DTYPE[q.dtype],
-        int(partition_tokens), ws_ptr, ws_len, _stream(q))
+        int(num_splits), ws_ptr, ws_len, _stream(q))
     if rc != 0:
         raise PkvError("paged_decode_attention", rc)
     return out

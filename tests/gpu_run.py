@@ -21,7 +21,7 @@ class GpuResult:
     prefill: Optional[torch.Tensor]
 
 
-def run(w: W.Workload, dev="cuda:0", partition_tokens=0, append=True, do_decode=True,
+def run(w: W.Workload, dev="cuda:0", num_splits=0, append=True, do_decode=True,
         do_prefill=True) -> GpuResult:
     kc = w.k_cache.to(dev)
     vc = w.v_cache.to(dev)
@@ -35,7 +35,7 @@ def run(w: W.Workload, dev="cuda:0", partition_tokens=0, append=True, do_decode=
     if do_decode and w.B:
         dec = ops.paged_decode_attention(
             w.dec_q.to(dev), kc, vc, w.dec_block_tables.to(dev), w.dec_context_lens.to(dev),
-            w.dec_max_context_len, scale=w.scale, partition_tokens=partition_tokens)
+            w.dec_max_context_len, scale=w.scale, num_splits=num_splits)
     torch.cuda.synchronize()
     return GpuResult(kc.cpu(), vc.cpu(), None if dec is None else dec.cpu(),
                      None if pre is None else pre.cpu())

@@ -70,13 +70,13 @@ DECODE_GRID = [
 
 
 @pytest.mark.parametrize("dtype,d,h_q,h_kv", DECODE_GRID)
-@pytest.mark.parametrize("P", [0, 16, 112])
-def test_decode_grid(dtype, d, h_q, h_kv, P):
+@pytest.mark.parametrize("splits", [0, 1, 13, 300])
+def test_decode_grid(dtype, d, h_q, h_kv, splits):
     rng = np.random.default_rng(1000 + d + h_q * 7 + h_kv)
     lens = [1, 15, 16, 17, 63, 64, 65, 200, 333, 700]
     w = W.build("grid", rng, dtype=dtype, h_q=h_q, h_kv=h_kv, d=d, decode_lens=lens,
                 free_frac=0.2, max_blocks_per_seq=50, poison=True)
-    res = run(w, DEV, partition_tokens=P)
+    res = run(w, DEV, num_splits=splits)
     kc_ref, vc_ref = check_append(w, res)
     check_decode(w, res, kc_ref, vc_ref)
 
@@ -104,13 +104,13 @@ def test_decode_zero_length_and_single_token():
     assert max_err(out, ref) <= TOL[w.dtype]
 
 
-@pytest.mark.parametrize("P", [16, 32, 48, 64, 128, 256, 512, 1024])
-def test_decode_partition_invariance(P):
+@pytest.mark.parametrize("splits", [1, 2, 3, 17, 64, 500, 2048, 5000])
+def test_decode_split_invariance(splits):
     rng = np.random.default_rng(77)
     lens = rng.integers(1, 3000, size=12)
     w = W.build("pinv", rng, dtype="bf16", h_q=32, h_kv=8, d=128, decode_lens=lens,
                 free_frac=0.1, poison=True)
-    res = run(w, DEV, partition_tokens=P)
+    res = run(w, DEV, num_splits=splits)
     kc_ref, vc_ref = check_append(w, res)
     check_decode(w, res, kc_ref, vc_ref)
 
@@ -122,10 +122,10 @@ def _pool_from_logical(Ks, Vs, seed, dtype, extra=5, prefix_share=0):
             torch.from_numpy(t))
 
 
-def _decode_gpu(q, kc, vc, t, lens, P, scale):
+def _decode_gpu(q, kc, vc, t, lens, splits, scale):
     out = ops.paged_decode_attention(q.to(DEV), kc.to(DEV), vc.to(DEV), t.to(DEV),
                                      torch.tensor(lens, dtype=torch.int32).to(DEV), max(lens),
-                                     scale=scale, partition_tokens=P)
+                                     scale=scale, num_splits=splits)
     return out.cpu()
 
 
@@ -149,7 +149,11 @@ def test_decode_block_permutation_bit_exact(dtype):
     assert max_err(oa, ref) <= TOL[dtype]
 
 
-def test_decode_prefix_sharing_and_batch_invariance_bit_exact():
+def test_decode_prefix_sharing_and_batch_invariance():
+    """Shared prefix blocks give the same bits as private copies (same work
+    layout).  Batched equals single: bit-exact when each sequence is reduced by
+    one wave (num_splits=1), within tolerance for any split, since the split of
+    a sequence across waves depends on the rest of the batch."""
     rng = np.random.default_rng(9)
     P_blocks = 13
     pk = rng.standard_normal((P_blocks * 16, 8, 128))
@@ -161,13 +165,20 @@ def test_decode_prefix_sharing_and_batch_invariance_bit_exact():
     shared = _pool_from_logical(Ks, Vs, 3, torch.bfloat16, prefix_share=P_blocks)
     private = _pool_from_logical(Ks, Vs, 4, torch.bfloat16)
     assert torch.equal(shared[2][1:, :P_blocks], shared[2][:1, :P_blocks].expand(3, -1))
-    o_sh = _decode_gpu(q, *shared, lens, 256, 0.0883883476)
-    o_pr = _decode_gpu(q, *private, lens, 256, 0.0883883476)
-    assert torch.equal(bits(o_sh), bits(o_pr))
-    for b in range(len(lens)):
-        one = _decode_gpu(q[b:b + 1], shared[0], shared[1], shared[2][b:b + 1], [lens[b]], 256,
-                          0.0883883476)
-        assert torch.equal(bits(one[0]), bits(o_sh[b]))
+    scale = 0.0883883476
+    ref = O.decode(q.double().numpy(), shared[0].double().numpy(), shared[1].double().numpy(),
+                   shared[2].numpy(), lens, scale)
+    for splits in (0, 1, 256):
+        o_sh = _decode_gpu(q, *shared, lens, splits, scale)
+        o_pr = _decode_gpu(q, *private, lens, splits, scale)
+        assert torch.equal(bits(o_sh), bits(o_pr))
+        assert max_err(o_sh, ref) <= 2e-2
+        for b in range(len(lens)):
+            one = _decode_gpu(q[b:b + 1], shared[0], shared[1], shared[2][b:b + 1], [lens[b]],
+                              splits, scale)
+            if splits == 1:
+                assert torch.equal(bits(one[0]), bits(o_sh[b]))
+            assert max_err(one, ref[b:b + 1]) <= 2e-2
 
 
 # ----------------------------------------------------------------------------- prefill coverage

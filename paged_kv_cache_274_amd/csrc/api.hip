@@ -164,6 +164,9 @@ int paged_decode_attention(void* out, const void* q, const void* k_cache, const 
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.ws = (float*)workspace;
+  a.seg_desc = (int32_t*)((char*)workspace + pkv::decode_partials_bytes(B, h_q, h_kv, d_h, bf16,
+                                                                         max_context_len, num_splits));
+  a.line_total = (int64_t*)((char*)workspace + need - 16);
   a.B = B;
   a.h_q = h_q;
   a.h_kv = h_kv;

@@ -49,9 +49,7 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units
 #define PKV_DECODE_DEPTH 2
 #endif
 constexpr int kDepth = PKV_DECODE_DEPTH;  // K/V blocks a wave holds in registers
-#ifndef PKV_DECODE_WAVES_PER_SIMD
-#define PKV_DECODE_WAVES_PER_SIMD 2
-#endif
+
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // Lane mapping.  A token row of D elements is covered by kLPT adjacent lanes,
@@ -327,110 +325,197 @@ __device__ __forceinline__ ScanResult scan_blocks(const DecodeArgs& a, int b, in
   return r;
 }
 
+// Merges the partial states of head j of one segment cut by range boundaries
+// with the exact log-sum-exp rule and stores the normalised result.  The pieces
+// are wave wa's last-segment slot and the first-segment slots of the non-empty
+// waves wa + 1 .. wb (all waves are non-empty when the line has at least as many
+// blocks as splits).  Run by one whole wave.  The pieces' (max, sum) and the
+// first eight pieces' accumulators are requested together, before any of them
+// is used, so a merge of up to eight pieces costs one memory round trip.
 template <typename T, int D, int GC>
-struct Segment {
+__device__ __forceinline__ void merge_segment_head(const DecodeArgs& a, const Line& line, int b,
+                                                   int head0, int j, int wa, int wb, int lane) {
+  const int np = wb - wa + 1;
+  const bool all_live = line.total >= line.splits;
+  constexpr int CPL = (D + kWave - 1) / kWave;  // channels per lane
+  constexpr int kBatch = 8;
+  auto piece = [&](int k) -> const float* {
+    return a.ws + ((size_t)((wa + k) * 2 + (k == 0 ? 1 : 0)) * GC + j) * (D + 2);
+  };
+  auto live = [&](int k) -> bool {
+    return all_live || k == 0 || line.start(wa + k) < line.start(wa + k + 1);
+  };
+  auto load_batch = [&](int k0, uint64_t live_mask, float (&x)[kBatch][CPL]) {
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const bool use = k0 + t < np && ((live_mask >> (t & 63)) & 1);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = lane + i * kWave;
+        x[t][i] = (use && c < D) ? piece(k0 + t)[c] : 0.f;
+      }
+    }
+  };
+  float o[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) o[i] = 0.f;
+  float inv;
+  if (np <= kWave) {
+    const bool lk = lane < np && live(lane);
+    const uint64_t live_mask = __ballot(lk);
+    const float mk = lk ? piece(lane)[D] : kNegInf;
+    const float lv = lk ? piece(lane)[D + 1] : 0.f;
+    float x[kBatch][CPL];
+    load_batch(0, live_mask, x);
+    const float M = wave_max(mk);
+    const float wk = lk ? fast_exp2(mk - M) : 0.f;
+    inv = 1.f / wave_sum(wk * lv);
+    for (int k0 = 0; k0 < np; k0 += kBatch) {
+      if (k0 > 0) load_batch(k0, live_mask >> k0, x);
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        const float w = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(wk), min(k0 + t, kWave - 1)));
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) o[i] = fmaf(w, x[t][i], o[i]);
+      }
+    }
+  } else {
+    float M = kNegInf;
+    for (int k0 = 0; k0 < np; k0 += kWave) {
+      const int k = k0 + lane;
+      M = fmaxf(M, wave_max((k < np && live(k)) ? piece(k)[D] : kNegInf));
+    }
+    float ls = 0.f;
+    for (int k0 = 0; k0 < np; k0 += kWave) {
+      const int k = k0 + lane;
+      const bool lk = k < np && live(k);
+      const float wk = lk ? fast_exp2(piece(k)[D] - M) : 0.f;
+      ls += wave_sum(lk ? wk * piece(k)[D + 1] : 0.f);
+      const uint64_t live_mask = __ballot(lk);
+      const int kn = min(kWave, np - k0);
+      for (int t0 = 0; t0 < kn; t0 += kBatch) {
+        float x[kBatch][CPL];
+        load_batch(k0 + t0, t0 + kBatch <= kWave ? live_mask >> t0 : 0, x);
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t) {
+          const float w = __int_as_float(
+              __builtin_amdgcn_readlane(__float_as_int(wk), min(t0 + t, kWave - 1)));
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) o[i] = fmaf(t0 + t < kn ? w : 0.f, x[t][i], o[i]);
+        }
+      }
+    }
+    inv = 1.f / ls;
+  }
+  T* out = reinterpret_cast<T*>(a.out) + ((size_t)b * a.h_q + head0 + j) * D;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + i * kWave;
+    if (c < D) store_elem<T>(out, c, o[i] * inv);
+  }
+}
+
+// A piece of a wave's range: blocks j0 .. j1-1 of segment (b, kc), whose block
+// 0 sits at line position seg0.
+struct Piece {
+  int b, kc, j0, j1, nb;
+  int64_t seg0;
+  bool valid;
+};
+
+// The piece after p on a wave's range ending at e (wave-uniform).
+__device__ __forceinline__ Piece next_piece(const DecodeArgs& a, int HC, const Piece& p, int64_t e) {
+  Piece n = p;
+  n.valid = false;
+  if (p.seg0 + p.j1 >= e) return n;
+  if (p.kc + 1 < HC) {
+    n.kc = p.kc + 1;
+    n.seg0 = p.seg0 + p.nb;
+  } else {
+    int b = p.b, nb = 0;
+    do {
+      ++b;
+      nb = b < a.B ? seq_blocks(a, b) : 1;
+    } while (nb == 0);
+    if (b >= a.B) return n;  // only reachable if the lengths changed under the kernel
+    n.b = b;
+    n.kc = 0;
+    n.nb = nb;
+    n.seg0 = p.seg0 + p.nb;
+  }
+  n.j0 = 0;
+  n.j1 = (int)min((int64_t)n.nb, e - n.seg0);
+  n.valid = true;
+  return n;
+}
+
+// Streams one wave's range of the line.  The K/V block pipeline runs through
+// the whole range without draining at piece boundaries: the next piece's
+// query registers and first table entry are requested when a piece starts, and
+// its first block is loaded before the current piece's epilogue, whose
+// reductions and stores then hide that load.  Table entries are read with
+// scalar loads one block ahead, so they never hold up the vector loads.
+template <typename T, int D, int GC>
+struct RangeStream {
   using Sh = DecodeShape<T, D>;
   static constexpr int VPL = Sh::kVPL;
   static constexpr int EPL = Sh::kEPL;
 
-  // Attends blocks j0 .. j1-1 of segment (b, kc) and stores the result: the
-  // normalised output if the piece is the whole segment, else a partial state
-  // in slot `slot` of wave W.
-  __device__ static void run(const DecodeArgs& a, int W, int b, int kc, int j0, int j1, int nb,
-                             int lane) {
-    const int sub = lane % Sh::kLPT;
-    const int slot_id = lane / Sh::kLPT;
-    const int kvh = kc / a.n_chunks;
-    const int chunk = kc - kvh * a.n_chunks;
-    const int head0 = kvh * a.g + chunk * GC;
-    const int nh = min(GC, a.g - chunk * GC);
-    const int L = seq_len(a, b);
+  struct Ctx {  // per-piece constants (wave-uniform)
+    int kvh, head0, nh, L;
+    const int32_t* trow;
+  };
 
-    QRegs<GC, VPL> q;
-    {
-      const uint4* qv = reinterpret_cast<const uint4*>(a.q);
-#pragma unroll
-      for (int j = 0; j < GC; ++j) {
-        const int h = head0 + min(j, nh - 1);
-        const size_t rowv = ((size_t)b * a.h_q + h) * Sh::kRowVec;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          const uint4 x = qv[rowv + v * Sh::kLPT + sub];
-          q.w[j][v * 4 + 0] = x.x;
-          q.w[j][v * 4 + 1] = x.y;
-          q.w[j][v * 4 + 2] = x.z;
-          q.w[j][v * 4 + 3] = x.w;
-        }
-      }
-    }
-    float m[GC], l[GC], acc[GC][EPL];
+  __device__ static Ctx ctx_of(const DecodeArgs& a, const Piece& p) {
+    Ctx c;
+    c.kvh = p.kc / a.n_chunks;
+    const int chunk = p.kc - c.kvh * a.n_chunks;
+    c.head0 = c.kvh * a.g + chunk * GC;
+    c.nh = min(GC, a.g - chunk * GC);
+    c.L = seq_len(a, p.b);
+    c.trow = a.block_tables + (size_t)p.b * a.max_blocks_per_seq;
+    return c;
+  }
+
+  __device__ static int table_entry(const DecodeArgs& a, const Ctx& c, int j) {
+    const int e = c.trow[j];
+    return (e >= 0 && e < a.n_blocks) ? e : 0;
+  }
+
+  __device__ static void load_q(const DecodeArgs& a, const Piece& p, const Ctx& c, int sub,
+                                QRegs<GC, VPL>& q) {
+    const uint4* qv = reinterpret_cast<const uint4*>(a.q);
 #pragma unroll
     for (int j = 0; j < GC; ++j) {
-      m[j] = kNegInf;
-      l[j] = 0.f;
+      const int h = c.head0 + min(j, c.nh - 1);
+      const size_t rowv = ((size_t)p.b * a.h_q + h) * Sh::kRowVec;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
-    }
-
-    const uint4* kc4 = reinterpret_cast<const uint4*>(a.k_cache);
-    const uint4* vc4 = reinterpret_cast<const uint4*>(a.v_cache);
-    const size_t head_vecs = (size_t)kBlock * Sh::kRowVec;
-    const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-
-    for (int jb = j0; jb < j1; jb += kWave) {
-      const int n = min(j1 - jb, kWave);
-      int tbl = 0;
-      if (lane < n) {
-        const int e = trow[jb + lane];
-        tbl = (e >= 0 && e < a.n_blocks) ? e : 0;
-      }
-      auto base_of = [&](int t) -> size_t {
-        const int blk = __builtin_amdgcn_readlane(tbl, t);
-        return ((size_t)blk * a.h_kv + kvh) * head_vecs;
-      };
-      auto attend_last = [&](const BlockOf<T, D>& r, int t) {
-        const int valid = L - (jb + t) * kBlock;
-        if (valid >= kBlock)
-          attend_block<T, D, GC, false>(r, q, m, l, acc, a.scale_log2, slot_id, kBlock);
-        else
-          attend_block<T, D, GC, true>(r, q, m, l, acc, a.scale_log2, slot_id, valid);
-      };
-      auto load_t = [&](BlockOf<T, D>& r, int t) {
-        const size_t base = base_of(t);
-        load_block<T, D>(r, kc4 + base, vc4 + base, slot_id, sub);
-      };
-      // Software pipeline: kDepth blocks in registers, kDepth - 1 of them in
-      // flight while one is used.  Only the last block of a run can be the
-      // partial last block of a sequence.
-      BlockOf<T, D> R[kDepth];
-#pragma unroll
-      for (int i = 0; i < kDepth - 1; ++i)
-        if (i < n) load_t(R[i], i);
-      int t = 0;
-      while (t + 2 * kDepth - 2 < n) {
-#pragma unroll
-        for (int u = 0; u < kDepth; ++u) {
-          load_t(R[(u + kDepth - 1) % kDepth], t + u + kDepth - 1);
-          attend_block<T, D, GC, false>(R[u], q, m, l, acc, a.scale_log2, slot_id, kBlock);
-        }
-        t += kDepth;
-      }
-      // At most 2 * kDepth - 2 blocks remain; block t + v is in R[v % kDepth].
-#pragma unroll
-      for (int u = 0; u < 2 * kDepth - 2; ++u) {
-        if (t + u < n) {
-          if (t + u + kDepth - 1 < n) load_t(R[(u + kDepth - 1) % kDepth], t + u + kDepth - 1);
-          if (t + u + 1 < n)
-            attend_block<T, D, GC, false>(R[u % kDepth], q, m, l, acc, a.scale_log2, slot_id, kBlock);
-          else
-            attend_last(R[u % kDepth], t + u);
-        }
+      for (int v = 0; v < VPL; ++v) {
+        const uint4 x = qv[rowv + v * Sh::kLPT + sub];
+        q.w[j][v * 4 + 0] = x.x;
+        q.w[j][v * 4 + 1] = x.y;
+        q.w[j][v * 4 + 2] = x.z;
+        q.w[j][v * 4 + 3] = x.w;
       }
     }
+  }
 
-    // Merge the lanes' states: lanes with the same sub hold the same channels.
-    const bool whole = (j0 == 0 && j1 == nb);
-    const int slot = j0 > 0 ? 0 : 1;
+  // Stores a finished piece: the normalised output if it is the whole
+  // segment, else a partial state in slot 0 (first piece of the wave's range)
+  // or 1 (last).  The wave holding a segment's first block records which waves
+  // hold its pieces, for the second pass.
+  __device__ static void epilogue(const DecodeArgs& a, const Line& line, int W, const Piece& p,
+                                  const Ctx& c, int lane, float (&m)[GC], float (&l)[GC],
+                                  float (&acc)[GC][EPL]) {
+    const int sub = lane % Sh::kLPT;
+    const int slot_id = lane / Sh::kLPT;
+    const bool whole = (p.j0 == 0 && p.j1 == p.nb);
+    const int slot = p.j0 > 0 ? 0 : 1;
+    if (p.j0 == 0 && lane == 0) {
+      const int wb = whole ? W : line.wave_of(p.seg0 + p.nb - 1);
+      reinterpret_cast<int2*>(a.seg_desc)[(size_t)p.b * a.h_kv * a.n_chunks + p.kc] = make_int2(W, wb);
+    }
 #pragma unroll
     for (int j = 0; j < GC; ++j) {
       const float M = class_max<Sh::kLPT>(m[j]);
@@ -438,10 +523,10 @@ struct Segment {
       const float ls = class_sum<Sh::kLPT>(l[j] * f);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[j][e] = class_sum<Sh::kLPT>(acc[j][e] * f);
-      if (j >= nh || slot_id != 0) continue;
+      if (j >= c.nh || slot_id != 0) continue;
       if (whole) {
         const float inv = 1.f / ls;
-        T* out = reinterpret_cast<T*>(a.out) + ((size_t)b * a.h_q + head0 + j) * D;
+        T* out = reinterpret_cast<T*>(a.out) + ((size_t)p.b * a.h_q + c.head0 + j) * D;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) store_elem<T>(out, lane_channel<T, D>(sub, e), acc[j][e] * inv);
       } else {
@@ -455,27 +540,140 @@ struct Segment {
       }
     }
   }
+
+  __device__ static void run(const DecodeArgs& a, const Line& line, int W, int64_t e, Piece cur,
+                             int lane) {
+    const int HC = a.h_kv * a.n_chunks;
+    const int sub = lane % Sh::kLPT;
+    const int slot_id = lane / Sh::kLPT;
+    const uint4* kc4 = reinterpret_cast<const uint4*>(a.k_cache);
+    const uint4* vc4 = reinterpret_cast<const uint4*>(a.v_cache);
+    const size_t head_vecs = (size_t)kBlock * Sh::kRowVec;
+
+    Ctx cc = ctx_of(a, cur);
+    QRegs<GC, VPL> q, qn;
+    load_q(a, cur, cc, sub, q);
+    Piece nxt = next_piece(a, HC, cur, e);
+    Ctx nc = nxt.valid ? ctx_of(a, nxt) : cc;
+    int nxt_blk = 0;
+    if (nxt.valid) {
+      load_q(a, nxt, nc, sub, qn);
+      nxt_blk = table_entry(a, nc, 0);
+    }
+
+    float m[GC], l[GC], acc[GC][EPL];
+    auto reset = [&]() {
+#pragma unroll
+      for (int j = 0; j < GC; ++j) {
+        m[j] = kNegInf;
+        l[j] = 0.f;
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) acc[j][x] = 0.f;
+      }
+    };
+    reset();
+
+    int t = cur.j0;
+    int blk_next = cur.j0 + 1 < cur.j1 ? table_entry(a, cc, cur.j0 + 1) : 0;  // one block ahead
+    BlockOf<T, D> A, B;
+    {
+      const size_t base = ((size_t)table_entry(a, cc, cur.j0) * a.h_kv + cc.kvh) * head_vecs;
+      load_block<T, D>(A, kc4 + base, vc4 + base, slot_id, sub);
+    }
+
+    // Attends block t (in X) after loading the following block into Y: the
+    // next block of this piece, else the next piece's first block, else a
+    // cache-resident dummy (so that the loop's loads are unconditional).
+    // Returns true when block t was the piece's last.
+    auto step = [&](BlockOf<T, D>& X, BlockOf<T, D>& Y) -> bool {
+      const bool more = t + 1 < cur.j1;
+      int blk, kvh, sl = slot_id, sb = sub;
+      if (more) {
+        blk = blk_next;
+        kvh = cc.kvh;
+      } else if (nxt.valid) {
+        blk = nxt_blk;
+        kvh = nc.kvh;
+      } else {
+        blk = 0;
+        kvh = 0;
+        sl = 0;
+        sb = 0;
+      }
+      const size_t base = ((size_t)blk * a.h_kv + kvh) * head_vecs;
+      load_block<T, D>(Y, kc4 + base, vc4 + base, sl, sb);
+      if (t + 2 < cur.j1) blk_next = table_entry(a, cc, t + 2);
+      const int valid = cc.L - t * kBlock;
+      if (valid >= kBlock)
+        attend_block<T, D, GC, false>(X, q, m, l, acc, a.scale_log2, slot_id, kBlock);
+      else
+        attend_block<T, D, GC, true>(X, q, m, l, acc, a.scale_log2, slot_id, valid);
+      if (more) ++t;
+      return !more;
+    };
+
+    while (true) {
+      bool in_b;
+      while (true) {
+        if (step(A, B)) {
+          in_b = true;
+          break;
+        }
+        if (step(B, A)) {
+          in_b = false;
+          break;
+        }
+      }
+      epilogue(a, line, W, cur, cc, lane, m, l, acc);
+      if (!nxt.valid) break;
+      if (in_b) A = B;  // after the epilogue, so that the load has had time to land
+      cur = nxt;
+      cc = nc;
+#pragma unroll
+      for (int j = 0; j < GC; ++j)
+#pragma unroll
+        for (int x = 0; x < VPL * 4; ++x) q.w[j][x] = qn.w[j][x];
+      reset();
+      t = 0;
+      blk_next = cur.j1 > 1 ? table_entry(a, cc, 1) : 0;
+      nxt = next_piece(a, HC, cur, e);
+      if (nxt.valid) {
+        nc = ctx_of(a, nxt);
+        load_q(a, nxt, nc, sub, qn);
+        nxt_blk = table_entry(a, nc, 0);
+      }
+    }
+  }
 };
 
 template <typename T, int D, int GC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_SIMD))) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int W = blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (W >= a.num_splits) return;
   const int HC = a.h_kv * a.n_chunks;
 
+  // Sequences of length 0 get an all-zero output (sequence b by wave b mod splits).
+  for (int b0 = W; b0 < a.B; b0 += a.num_splits) {
+    if (seq_len(a, b0) != 0) continue;
+    T* out = reinterpret_cast<T*>(a.out) + (size_t)b0 * a.h_q * D;
+    for (int i = lane; i < a.h_q * D; i += kWave) store_elem<T>(out, i, 0.f);
+  }
+
   const ScanResult all = scan_blocks(a, -1, lane);
   const Line line{all.total * HC, a.num_splits};
+  if (W == 0 && lane == 0) *a.line_total = line.total;  // for the second pass
   if (line.total == 0) return;
   const int64_t s = line.start(W);
   const int64_t e = line.start(W + 1);
   if (s >= e) return;
 
   // The sequence holding position s: the first whose end lies past s.
-  int b = 0, nb = 0;
-  int64_t seq0 = 0;
+  Piece first;
   {
     int64_t base = 0;
+    int b = 0, nb = 1;
+    int64_t seq0 = 0;
     for (int c0 = 0; c0 < a.B; c0 += kWave) {
       const int bb = c0 + lane;
       const int n = bb < a.B ? seq_blocks(a, bb) : 0;
@@ -490,33 +688,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_
       }
       base += __shfl(incl, kWave - 1);
     }
+    const int64_t r = s - seq0;
+    first.b = b;
+    first.nb = nb;
+    first.kc = (int)(r / nb);
+    first.j0 = (int)(r - (int64_t)first.kc * nb);
+    first.seg0 = seq0 + (int64_t)first.kc * nb;
+    first.j1 = (int)min((int64_t)nb, e - first.seg0);
+    first.valid = true;
   }
-
-  int64_t pos = s;
-  while (true) {
-    const int64_t r = pos - seq0;
-    const int kc = (int)(r / nb);
-    const int j0 = (int)(r - (int64_t)kc * nb);
-    const int64_t seg0 = seq0 + (int64_t)kc * nb;
-    const int j1 = (int)min((int64_t)nb, e - seg0);
-    Segment<T, D, GC>::run(a, W, b, kc, j0, j1, nb, lane);
-    pos = seg0 + j1;
-    if (pos >= e) break;
-    if (kc + 1 < HC) continue;  // next head chunk of the same sequence
-    seq0 += (int64_t)HC * nb;
-    do {
-      ++b;
-      nb = b < a.B ? seq_blocks(a, b) : 1;
-    } while (nb == 0);
-    if (b >= a.B) break;  // only reachable if the lengths changed under the kernel
-  }
+  RangeStream<T, D, GC>::run(a, line, W, e, first, lane);
 }
 
-// Merges the partial states of segments cut by range boundaries (exact
-// log-sum-exp), and writes zeros for sequences of length 0.  One workgroup per
-// segment; wave j takes heads j, j + 4, ...  Each pass over the pieces issues
-// all of its loads before using them, so a merge costs a few memory round
-// trips whatever the number of pieces.
+// Second pass: merges the segments cut by range boundaries.  One workgroup per
+// segment; wave j takes heads j, j + 4, ...
 constexpr int kCombineWaves = 4;
 template <typename T, int D, int GC>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
@@ -530,79 +715,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int chunk = kc - kvh * a.n_chunks;
   const int head0 = kvh * a.g + chunk * GC;
   const int nh = min(GC, a.g - chunk * GC);
-  T* out = reinterpret_cast<T*>(a.out);
-
   const int nb = seq_blocks(a, b);
-  if (nb == 0) {
-    for (int i = threadIdx.x; i < nh * D; i += blockDim.x)
-      store_elem<T>(out, ((size_t)b * a.h_q + head0 + i / D) * D + i % D, 0.f);
-    return;
-  }
-  const ScanResult sc = scan_blocks(a, b, lane);
-  const Line line{sc.total * HC, a.num_splits};
-  const int64_t S0 = sc.before * HC + (int64_t)kc * nb;
-  const int wa = line.wave_of(S0);
-  const int wb = line.wave_of(S0 + nb - 1);
-  if (wa == wb) return;  // stored whole by its wave
-  const int np = wb - wa + 1;
-  constexpr int CPL = (D + kWave - 1) / kWave;  // channels per lane
-
-  for (int j = wave; j < nh; j += kCombineWaves) {
-    // Piece k is wave wa + k: slot 1 for the first, slot 0 for later non-empty waves.
-    auto piece = [&](int k) -> const float* {
-      return a.ws + ((size_t)((wa + k) * 2 + (k == 0 ? 1 : 0)) * GC + j) * (D + 2);
-    };
-    auto live = [&](int k) -> bool {
-      return k == 0 || line.start(wa + k) < line.start(wa + k + 1);
-    };
-    float M = kNegInf;
-    for (int k0 = 0; k0 < np; k0 += kWave) {
-      const int k = k0 + lane;
-      M = fmaxf(M, wave_max((k < np && live(k)) ? piece(k)[D] : kNegInf));
-    }
-    float ls = 0.f;
-    for (int k0 = 0; k0 < np; k0 += kWave) {
-      const int k = k0 + lane;
-      float x = 0.f;
-      if (k < np && live(k)) x = fast_exp2(piece(k)[D] - M) * piece(k)[D + 1];
-      ls += wave_sum(x);
-    }
-    const float inv = 1.f / ls;
-    float o[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) o[i] = 0.f;
-    for (int k0 = 0; k0 < np; k0 += kWave) {
-      const int k = k0 + lane;
-      const bool lk = k < np && live(k);
-      const uint64_t live_mask = __ballot(lk);  // pieces of empty waves are never read
-      const float wk = lk ? fast_exp2(piece(k)[D] - M) : 0.f;
-      const int kn = min(kWave, np - k0);
-      for (int t0 = 0; t0 < kn; t0 += 8) {
-        float x[8][CPL];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bool use = t0 + t < kn && ((live_mask >> (t0 + t)) & 1);
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) {
-            const int c = lane + i * kWave;
-            x[t][i] = (use && c < D) ? piece(k0 + t0 + t)[c] : 0.f;
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float w = __int_as_float(
-              __builtin_amdgcn_readlane(__float_as_int(wk), min(t0 + t, kWave - 1)));
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) o[i] = fmaf(w, x[t][i], o[i]);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = lane + i * kWave;
-      if (c < D) store_elem<T>(out, ((size_t)b * a.h_q + head0 + j) * D + c, o[i] * inv);
-    }
-  }
+  const int2 wr = reinterpret_cast<const int2*>(a.seg_desc)[seg];
+  if (nb == 0 || wr.x == wr.y) return;  // zero-filled, or stored whole, by the first pass
+  const Line line{*a.line_total, a.num_splits};
+  const int wa = wr.x;
+  const int wb = wr.y;
+  for (int j = wave; j < nh; j += kCombineWaves)
+    merge_segment_head<T, D, GC>(a, line, b, head0, j, wa, wb, lane);
 }
 
 template <typename T, int D, int GC>

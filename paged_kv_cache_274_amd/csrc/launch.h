@@ -45,14 +45,22 @@ inline int64_t decode_split_bound(int B, int h_q, int h_kv, int d_h, bool bf16,
   return up < 1 ? 1 : (up > kMaxAutoSplits ? kMaxAutoSplits : up);
 }
 
-// Per split: two partial states (first and last segment piece) of gc heads,
-// each d_h accumulators plus the running max and sum, in fp32.
-inline size_t decode_workspace_bytes(int B, int h_q, int h_kv, int d_h, bool bf16,
-                                     int max_context_len, int num_splits) {
-  if (B <= 0) return 0;
+// Workspace: per split, two partial states (first and last segment piece) of gc
+// heads, each d_h accumulators plus the running max and sum, in fp32; then one
+// descriptor per (sequence, KV head, head chunk) segment: the first and last
+// wave holding a piece of it; then the line length (int64, 16 bytes reserved).
+inline size_t decode_partials_bytes(int B, int h_q, int h_kv, int d_h, bool bf16,
+                                    int max_context_len, int num_splits) {
   const int gc = head_chunks(h_q / h_kv, d_h, bf16).per_chunk;
   return (size_t)decode_split_bound(B, h_q, h_kv, d_h, bf16, max_context_len, num_splits) * 2 *
          gc * (size_t)(d_h + 2) * sizeof(float);
+}
+inline size_t decode_workspace_bytes(int B, int h_q, int h_kv, int d_h, bool bf16,
+                                     int max_context_len, int num_splits) {
+  if (B <= 0) return 0;
+  const size_t segs = (size_t)B * h_kv * head_chunks(h_q / h_kv, d_h, bf16).n_chunks;
+  return decode_partials_bytes(B, h_q, h_kv, d_h, bf16, max_context_len, num_splits) +
+         ((segs * 2 * sizeof(int32_t) + 15) / 16) * 16 + 16;
 }
 
 struct DecodeArgs {
@@ -63,6 +71,8 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   float* ws;  // [num_splits][2][gc][d_h + 2]: accumulators, max (log2 units), sum
+  int32_t* seg_desc;  // [B * h_kv * n_chunks][2]: first and last wave of each segment
+  int64_t* line_total;  // blocks on the line, written by the first pass
   int B, h_q, h_kv, g, n_chunks, gc, n_blocks, max_blocks_per_seq, num_splits;
   float scale_log2;  // scale * log2(e)
 };

@@ -81,7 +81,7 @@ def test_decode_validation():
     assert _decode(scale=float("nan")) == 1
     assert _decode(ws=None, P=16) == 3
     need = ops.decode_workspace_bytes(4, 8, 2, 128, 256, num_splits=16)
-    assert need == 16 * 2 * 4 * 130 * 4
+    assert need == 16 * 2 * 4 * 130 * 4 + 4 * 2 * 8 + 16   # partials, segment descriptors, header
     assert _decode(P=16, ws_bytes=need - 1) == 3
     assert _decode(ws=MISALIGNED, P=16) == 3
     assert _decode(B=0, out=None, q=None) == 0
@@ -119,8 +119,9 @@ def test_workspace_bound(B, h_q, h_kv, d, maxc, dtype):
     upper = B * h_kv * n_chunks * (-(-maxc // 16))
     auto = min(max(upper, 1), 4096)
     ws = lambda n: ops.decode_workspace_bytes(B, h_q, h_kv, d, maxc, dtype, n)
-    assert ws(0) == auto * 2 * gc * (d + 2) * 4
-    assert ws(37) == 37 * 2 * gc * (d + 2) * 4
+    desc = -(-(B * h_kv * n_chunks * 8) // 16) * 16 + 16
+    assert ws(0) == auto * 2 * gc * (d + 2) * 4 + desc
+    assert ws(37) == 37 * 2 * gc * (d + 2) * 4 + desc
     assert ws(-1) == 0
     assert ws((1 << 16) + 1) == 0
     assert ops.decode_num_splits(B, h_q, h_kv, d, maxc, dtype, num_splits=48) == 48

@@ -1,34 +1,46 @@
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3|4]
 
-A step is one pass of the path over the Llama-3-8B-shaped decode batch
-(B=64, contexts U[128,4096], h_q=32, h_kv=8, d_h=128, bf16, 16-token blocks,
-pool = used blocks + 10% free, shuffled): kv_append of the 64 new tokens, then
-paged_decode_attention over every context.  Inputs are seeded synthetic data
-already resident in HBM; three copies of the pool are rotated so that no step
-finds its KV data in the 256 MB Infinity Cache or the L2s left by the step
-before.  K steps are timed with wall clock between two synchronisations.
+A step is one pass of the path over the decode batch: kv_append of the batch's
+new tokens, then paged_decode_attention over every context.  The default
+workload is the Llama-3-8B-shaped batch (B=64, contexts U[128,4096], h_q=32,
+h_kv=8, d_h=128, bf16, 16-token blocks, pool = used blocks + 10% free,
+shuffled); --config 4 selects the long-context batch (B=8, L=8192, 13 shared
+prefix blocks).  Inputs are seeded synthetic data already resident in HBM;
+three copies of the pool are rotated so that no step finds its KV data in the
+256 MB Infinity Cache or the L2s left by the step before.  K steps are timed
+with wall clock between two synchronisations.
 
 Printed as one JSON line:
   value      KV bytes attended per second (GB/s), whole step (append + decode)
-  roofline   the decode call (its kernels timed by HIP events on the launch
-             stream) against the 8 TB/s HBM peak, algorithmic bytes per launch
-             = sum_b L_b * 2 * h_kv * d_h * 2 B (KV-cache footprint per token of
-             one layer, LLM Inference Server page, Required Mathematical
-             Concepts)
+  roofline   the decode call (its two kernels; HIP events on the launch stream
+             around K back-to-back calls after the timed steps, and around each
+             call inside the steps) against the 8 TB/s HBM peak; algorithmic bytes per
+             call = sum_b L_b * 2 * h_kv * d_h * 2 B (the KV-cache footprint
+             per token of one layer: LLM Inference Server page, Required
+             Mathematical Concepts); traffic = counter-measured HBM bytes per
+             call from the committed rocprofv3 summary, if the decode sources
+             still match the ones it was taken on
   prefill    paged_prefill_attention on the mixed Qwen2.5-0.5B-shaped batch
              (4 prompts x 512 tokens, h_q=14, h_kv=2, d_h=64) in TFLOP/s
-  cpu_baseline  the CPU oracle on the same decode step, on the host's cores.
+  cpu_baseline  the CPU oracle on the same decode step, on one host core.
+
+Counter runs and their summaries (written to profiles/):
+  python bench.py --profile decode|prefill --steps N    short run for rocprofv3
+  python bench.py --summarize stats|traffic|mfma ...    rocprofv3 CSV -> profiles/*.txt
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import statistics
 import sys
 import time
+from collections import defaultdict
 
 import numpy as np
 import torch
@@ -36,9 +48,39 @@ import torch
 from paged_kv_cache_274_amd import ops
 from paged_kv_cache_274_amd import workloads as W
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+SIMDS = 1024                     # 256 CUs x 4 SIMDs
 METRIC = "paged decode attention: KV GB/s read and % of HBM peak; prefill TFLOP/s"
+COPY_BYTES = 256 << 20           # plain device copy used to calibrate the byte counters
+
+SLUG = {3: "llama3-8b-decode-b64", 4: "long-context-prefix-decode-b8",
+        5: "qwen2.5-0.5b-prefill-4x512"}
+WORKLOAD = {
+    3: "llama3-8b-shaped decode step: B=64, contexts U[128,4096], h_q=32, h_kv=8, d_h=128, "
+       "bf16, 16-token blocks, shuffled pool +10% free",
+    4: "long-context decode step: B=8, L=8192 with 13 shared prefix blocks, h_q=32, h_kv=8, "
+       "d_h=128, bf16, 16-token blocks, shuffled pool",
+}
+_CSRC = os.path.join(ROOT, "paged_kv_cache_274_amd", "csrc")
+DECODE_SOURCES = ("decode.hip", "launch.h", "device_common.h", "api.hip")
+PREFILL_SOURCES = ("prefill.hip", "launch.h", "device_common.h", "api.hip")
+
+# The commands behind each committed summary (run from the repository root).
+CMD_STATS = ("TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d gpurun_out/prof_bench -o bench "
+             "--output-format csv -- python3 bench.py{args} > gpurun_out/prof_bench/bench.json")
+CMD_PMC = ("TMPDIR=/tmp timeout -s KILL 120 rocprofv3 --pmc {counters} -d gpurun_out/{dir} -o run "
+           "--output-format csv -- python3 bench.py --profile {what} --steps {steps}{args}")
+
+
+def digest(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(_CSRC, n), "rb") as f:
+            h.update(n.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def kv_bytes(w: W.Workload) -> int:
@@ -54,6 +96,10 @@ def prefill_flops(w: W.Workload) -> int:
         n = int(w.pre_cu_seqlens[s + 1] - w.pre_cu_seqlens[s])
         total_pairs += sum(L - n + i + 1 for i in range(n))
     return 4 * w.d * w.h_q * total_pairs
+
+
+def pct(xs, p):
+    return float(np.percentile(np.asarray(xs), p))
 
 
 class Resident:
@@ -98,18 +144,35 @@ def time_decode_step(r: Resident, steps: int, warmup: int):
         r.append(i)
         r.decode(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [(mk(), mk(), mk()) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
-        r.append(i)
         ev[i][0].record()
-        r.decode(i)
+        r.append(i)
         ev[i][1].record()
+        r.decode(i)
+        ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = [a.elapsed_time(b) for a, b in ev]
-    return wall, dec_ms
+    app_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    dec_ms = [b.elapsed_time(c) for _, b, c in ev]
+    return wall, app_ms, dec_ms
+
+
+def time_decode_calls(r: Resident, iters: int, warmup: int = 3):
+    """Average duration of one decode call, from two HIP events around `iters`
+    back-to-back calls on the launch stream (no per-call event overhead)."""
+    for i in range(warmup):
+        r.decode(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(iters):
+        r.decode(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
 
 
 def time_prefill(r: Resident, iters: int = 50, warmup: int = 5):
@@ -124,6 +187,24 @@ def time_prefill(r: Resident, iters: int = 50, warmup: int = 5):
         ev[i][1].record()
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in ev]
+
+
+def time_copy(dev: str, nbytes: int = 1 << 30, iters: int = 10):
+    """Device-to-device copy rate (read + write bytes / time) of a plain 1 GiB copy."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / iters / 1e3
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / t / 1e9
 
 
 def cpu_baseline(w: W.Workload, reps: int):
@@ -152,10 +233,197 @@ def cpu_baseline(w: W.Workload, reps: int):
     med = statistics.median(times)
     return {"value": round(kv_bytes(w) / med / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"whole decode step of the same workload (kv_append + decode, "
+            "sample": f"{reps} whole decode steps of the same workload (kv_append + decode, "
                       f"{w.B} sequences, {int(w.dec_context_lens.sum())} context tokens), "
-                      f"median of {reps} runs, float64 NumPy with BLAS pinned to 1 thread, "
+                      f"median, float64 NumPy with BLAS pinned to 1 thread, "
                       f"{sum(times):.1f} s total; host {os.cpu_count()} CPUs"}
+
+
+# ----------------------------------------------------------------------------
+# committed counter summaries
+
+
+def summary_path(k: int, kind: str) -> str:
+    return os.path.join(PROFILES, f"{'prefill' if k == 5 else 'decode'}_{SLUG[k]}_{kind}.txt")
+
+
+def read_summary_fields(path: str) -> dict:
+    """`key: value` lines of a committed summary (an empty dict if there is none)."""
+    out = {}
+    if not os.path.exists(path):
+        return out
+    with open(path) as f:
+        for line in f:
+            if line.startswith("# ") or ":" not in line:
+                continue
+            key, _, val = line.partition(":")
+            out[key.strip()] = val.strip()
+    return out
+
+
+def measured_traffic(k: int):
+    """HBM bytes per decode call from the counter summary, None if the kernel changed since."""
+    f = read_summary_fields(summary_path(k, "hbm_traffic"))
+    if f.get("decode_sources_sha256") != digest(DECODE_SOURCES):
+        return None
+    return int(f["hbm_bytes_per_call"])
+
+
+def measured_mfma():
+    f = read_summary_fields(summary_path(5, "mfma"))
+    if f.get("prefill_sources_sha256") != digest(PREFILL_SOURCES):
+        return None
+    return {"mfma_util_pct": float(f["mfma_util_pct"]),
+            "mfma_flops_per_call": int(float(f["mfma_flops_per_call"]))}
+
+
+def _dispatches(csv_path: str):
+    """{dispatch id: (kernel name, {counter: value})} from a rocprofv3 counter CSV."""
+    rows = defaultdict(lambda: ["", {}])
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            d = rows[int(r["Dispatch_Id"])]
+            d[0] = r["Kernel_Name"]
+            d[1][r["Counter_Name"]] = d[1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return {k: (v[0], v[1]) for k, v in sorted(rows.items())}
+
+
+def _avg(ds, key, counter):
+    vals = [c[counter] for name, c in ds.values() if key in name and counter in c]
+    return statistics.mean(vals), len(vals)
+
+
+def _calibration(ds, counter):
+    vals = [c[counter] for name, c in ds.values() if "copy" in name.lower() and counter in c]
+    raw = max(vals) * 1024.0
+    return raw, COPY_BYTES / raw
+
+
+def summarize_traffic(k, fetch_csv, write_csv, steps, extra):
+    w = W.config(k)
+    f = _dispatches(fetch_csv)
+    wr = _dispatches(write_csv)
+    f_raw, f_fac = _calibration(f, "FETCH_SIZE")
+    w_raw, w_fac = _calibration(wr, "WRITE_SIZE")
+    lines = []
+    total_f = total_w = 0.0
+    for key in ("decode_split_kernel", "decode_combine_kernel"):
+        fk, n_f = _avg(f, key, "FETCH_SIZE")
+        wk, n_w = _avg(wr, key, "WRITE_SIZE")
+        fb, wb = fk * 1024 * f_fac, wk * 1024 * w_fac
+        total_f += fb
+        total_w += wb
+        lines.append(f"#   {key:24s} FETCH_SIZE {fk:12.1f} KiB x {f_fac:.3f} = {fb / 1e6:9.3f} MB"
+                     f"   WRITE_SIZE {wk:10.1f} KiB x {w_fac:.3f} = {wb / 1e6:8.3f} MB"
+                     f"   ({n_f}/{n_w} dispatches)")
+    alg = kv_bytes(w)
+    text = [
+        f"# HBM traffic of one paged_decode_attention call ({WORKLOAD[k]})",
+        "# counters: rocprofv3 --pmc, one pass per counter, KiB per dispatch, averaged over the",
+        "# decode dispatches; each scaled by what the same counter reads for a plain device copy",
+        f"# of {COPY_BYTES} bytes in the same run (the largest *copy* dispatch).",
+        "# commands (repository root, on the GPU):",
+        "#   " + CMD_PMC.format(counters="FETCH_SIZE", dir="pmc_fetch", what="decode", steps=steps,
+                                args=extra),
+        "#   " + CMD_PMC.format(counters="WRITE_SIZE", dir="pmc_write", what="decode", steps=steps,
+                                args=extra),
+        f"#   python bench.py --summarize traffic{extra} --steps {steps} "
+        "gpurun_out/pmc_fetch/run_counter_collection.csv gpurun_out/pmc_write/run_counter_collection.csv",
+        f"# calibration: copy FETCH_SIZE reads {f_raw / 1e6:.3f} MB -> factor {f_fac:.4f}; "
+        f"WRITE_SIZE reads {w_raw / 1e6:.3f} MB -> factor {w_fac:.4f}",
+        *lines,
+        f"# algorithmic KV bytes per call {alg}; measured read / algorithmic = {total_f / alg:.4f}",
+        f"decode_sources_sha256: {digest(DECODE_SOURCES)}",
+        f"fetch_bytes_per_call: {int(round(total_f))}",
+        f"write_bytes_per_call: {int(round(total_w))}",
+        f"hbm_bytes_per_call: {int(round(total_f + total_w))}",
+        f"algorithmic_bytes_per_call: {alg}",
+    ]
+    return "\n".join(text) + "\n"
+
+
+def summarize_mfma(csv_path, steps):
+    w = W.config(5)
+    ds = _dispatches(csv_path)
+    util, n = _avg(ds, "prefill", "MfmaUtil")
+    flops, _ = _avg(ds, "prefill", "MfmaFlopsBF16")
+    alg = prefill_flops(w)
+    text = [
+        "# MFMA use of one paged_prefill_attention call (Qwen2.5-0.5B-shaped prefill: 4 prompts x",
+        "# 512 tokens, h_q=14, h_kv=2, d_h=64, causal, bf16)",
+        "# command (repository root, on the GPU):",
+        "#   " + CMD_PMC.format(counters="MfmaUtil MfmaFlopsBF16", dir="pmc_mfma", what="prefill",
+                                steps=steps, args=""),
+        f"#   python bench.py --summarize mfma --steps {steps} gpurun_out/pmc_mfma/run_counter_collection.csv",
+        "# MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), percent, per dispatch;",
+        "# MfmaFlopsBF16 = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, per dispatch.",
+        f"# {n} prefill dispatches; algorithmic flops per call {alg} (causal pairs incl. diagonal);",
+        f"# issued / algorithmic = {flops / alg:.3f} (tiles above the diagonal and padding rows)",
+        f"prefill_sources_sha256: {digest(PREFILL_SOURCES)}",
+        f"mfma_util_pct: {util:.3f}",
+        f"mfma_flops_per_call: {flops:.0f}",
+        f"algorithmic_flops_per_call: {alg}",
+    ]
+    return "\n".join(text) + "\n"
+
+
+def summarize_stats(stats_csv, bench_json, extra):
+    with open(bench_json) as f:
+        line = json.loads([s for s in f.read().splitlines() if s.startswith("{")][-1])
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            if "pkv::" in r["Name"]:
+                rows.append(r)
+    split = [r for r in rows if "decode_split_kernel" in r["Name"]]
+    comb = [r for r in rows if "decode_combine_kernel" in r["Name"]]
+    call_ns = sum(float(r["AverageNs"]) for r in split + comb)
+    text = [
+        f"# Kernel time of the benchmark run ({line['config']['workload']})",
+        "# command (repository root, on the GPU):",
+        "#   " + CMD_STATS.format(args=extra),
+        f"#   python bench.py --summarize stats{extra} gpurun_out/prof_bench/bench_kernel_stats.csv "
+        "gpurun_out/prof_bench/bench.json",
+        "# rocprofv3 kernel stats (pkv kernels only):",
+        f"#   {'calls':>6s} {'avg_ns':>12s} {'min_ns':>10s} {'max_ns':>10s}  name",
+    ]
+    for r in rows:
+        text.append(f"#   {int(r['Calls']):6d} {float(r['AverageNs']):12.1f} {int(r['MinNs']):10d} "
+                    f"{int(r['MaxNs']):10d}  {r['Name'][:110]}")
+    text += [
+        f"# decode call = split pass + combine pass averages: {call_ns / 1e3:.2f} us (rocprofv3);",
+        f"# HIP events in the same run: {line['roofline']['avg_us']} us per call over back-to-back "
+        f"calls, {line['roofline']['in_step_avg_us']} us around single calls inside the steps",
+        f"decode_call_rocprof_us: {call_ns / 1e3:.3f}",
+        f"decode_call_events_us: {line['roofline']['avg_us']}",
+        f"bench_value_GBps: {line['value']}",
+        f"roofline_frac: {line['roofline']['frac']}",
+    ]
+    return "\n".join(text) + "\n"
+
+
+# ----------------------------------------------------------------------------
+
+
+def profile_run(what: str, k: int, steps: int, dev: str):
+    """A short run for counter collection: a calibration copy, then `steps` calls."""
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    print(f"profile: calibration copy of {COPY_BYTES} bytes done", flush=True)
+    if what == "decode":
+        r = Resident(W.config(k), dev, copies=3)
+        for i in range(steps):
+            r.decode(i)
+    else:
+        r = Resident(W.config(5), dev)
+        r.append(0)
+        for i in range(steps):
+            r.prefill(i)
+    torch.cuda.synchronize()
+    print(f"profile: {steps} {what} calls done", flush=True)
 
 
 def main(argv=None):
@@ -163,10 +431,32 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, choices=(3, 4))
     ap.add_argument("--copies", type=int, default=3)
-    ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--cpu-reps", type=int, default=15)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", choices=("decode", "prefill"))
+    ap.add_argument("--summarize", choices=("stats", "traffic", "mfma"))
+    ap.add_argument("inputs", nargs="*")
     args = ap.parse_args(argv)
+    extra = "" if args.config == 3 else f" --config {args.config}"
+
+    if args.summarize:
+        os.makedirs(PROFILES, exist_ok=True)
+        if args.summarize == "traffic":
+            text = summarize_traffic(args.config, args.inputs[0], args.inputs[1], args.steps, extra)
+            path = summary_path(args.config, "hbm_traffic")
+        elif args.summarize == "mfma":
+            text = summarize_mfma(args.inputs[0], args.steps)
+            path = summary_path(5, "mfma")
+        else:
+            text = summarize_stats(args.inputs[0], args.inputs[1], extra)
+            path = summary_path(args.config, "kernel_stats")
+        with open(path, "w") as f:
+            f.write(text)
+        print(text, end="")
+        return 0
+
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(the per-GPU workload is already one GPU's share); run with --gpus 1",
@@ -177,15 +467,19 @@ def main(argv=None):
         return 1
     dev = "cuda:0"
     ops.lib()
+    if args.profile:
+        profile_run(args.profile, args.config, args.steps, dev)
+        return 0
 
-    w3 = W.config(3)
-    r3 = Resident(w3, dev, copies=args.copies)
-    wall, dec_ms = time_decode_step(r3, args.steps, args.warmup)
-    kvb = kv_bytes(w3)
+    wk = W.config(args.config)
+    rk = Resident(wk, dev, copies=args.copies)
+    wall, app_ms, dec_ms = time_decode_step(rk, args.steps, args.warmup)
+    kvb = kv_bytes(wk)
     value = kvb * args.steps / wall / 1e9
-    dec_avg_s = statistics.mean(dec_ms) / 1e3
+    dec_avg_s = time_decode_calls(rk, args.steps) / 1e3
     achieved = kvb / dec_avg_s / 1e9
-    del r3
+    app_bytes = 2 * wk.T * wk.h_kv * wk.d * wk.elem_bytes * 2 + wk.T * 8
+    del rk
     torch.cuda.empty_cache()
 
     w5 = W.config(5)
@@ -196,6 +490,10 @@ def main(argv=None):
     pf_tflops = prefill_flops(w5) / pf_avg_s / 1e12
     del r5
     torch.cuda.empty_cache()
+
+    copy_gbs = time_copy(dev)
+    traffic = measured_traffic(args.config)
+    mfma = measured_mfma()
 
     line = {
         "metric": METRIC,
@@ -211,13 +509,12 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), bf16)",
         "config": {
-            "workload": "llama3-8b-shaped decode step: B=64, contexts U[128,4096], h_q=32, "
-                        "h_kv=8, d_h=128, bf16, 16-token blocks, shuffled pool +10% free",
-            "context_tokens": int(w3.dec_context_lens.sum()),
+            "workload": WORKLOAD[args.config],
+            "context_tokens": int(wk.dec_context_lens.sum()),
             "kv_bytes_per_step": kvb,
-            "n_blocks": w3.n_blocks,
-            "num_splits": ops.decode_num_splits(w3.B, w3.h_q, w3.h_kv, w3.d,
-                                                w3.dec_max_context_len, w3.dtype),
+            "n_blocks": wk.n_blocks,
+            "num_splits": ops.decode_num_splits(wk.B, wk.h_q, wk.h_kv, wk.d,
+                                                wk.dec_max_context_len, wk.dtype),
             "pool_copies_rotated": args.copies,
         },
         "roofline": {
@@ -227,8 +524,20 @@ def main(argv=None):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "avg_us": round(dec_avg_s * 1e6, 2),
+            "in_step_avg_us": round(statistics.mean(dec_ms) * 1e3, 2),
+            "in_step_median_us": round(pct(dec_ms, 50) * 1e3, 2),
+            "in_step_p10_us": round(pct(dec_ms, 10) * 1e3, 2),
+            "in_step_p90_us": round(pct(dec_ms, 90) * 1e3, 2),
+            "copy_GBps": round(copy_gbs, 1),
+            "frac_of_copy": round(achieved / copy_gbs, 4),
+        },
+        "append": {
+            "tokens": wk.T,
+            "bytes": app_bytes,
+            "avg_us": round(statistics.mean(app_ms) * 1e3, 2),
+            "GBps": round(app_bytes / (statistics.mean(app_ms) / 1e3) / 1e9, 1),
         },
         "prefill": {
             "workload": "qwen2.5-0.5b-shaped prefill: 4 prompts x 512 tokens, h_q=14, h_kv=2, "
@@ -238,10 +547,11 @@ def main(argv=None):
             "tflops": round(pf_tflops, 3),
             "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
             "frac": round(pf_tflops / BF16_MFMA_PEAK_TFLOPS, 5),
+            "mfma_util_pct": None if mfma is None else mfma["mfma_util_pct"],
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w3, args.cpu_reps)
+        line["cpu_baseline"] = cpu_baseline(wk, args.cpu_reps)
     print(json.dumps(line), flush=True)
     return 0
 

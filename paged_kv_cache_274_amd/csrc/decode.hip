@@ -121,10 +121,7 @@ struct QRegs {
   uint32_t w[GC][VPL * 4];
 };
 
-__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
-  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
+
 
 // Folds one block into the lane's running (m, l, acc).  MASK: tokens at local
 // index >= valid lie past the context; their scores and values are ignored,
@@ -247,7 +244,7 @@ __device__ __forceinline__ void attend_block(const BlockOf<T, D>& r,
     for (int pr = 0; pr < NP / 2; ++pr) {
       uint32_t pp[GC];
 #pragma unroll
-      for (int j = 0; j < GC; ++j) pp[j] = bf16x2_bits(p[2 * pr][j], p[2 * pr + 1][j]);
+      for (int j = 0; j < GC; ++j) pp[j] = pack_bf16x2(p[2 * pr][j], p[2 * pr + 1][j]);
 #pragma unroll
       for (int v = 0; v < VPL; ++v)
 #pragma unroll
@@ -283,7 +280,7 @@ __device__ __forceinline__ void store_elem(T* out, size_t i, float x) {
 
 // Clamped context length: never beyond the block table row.
 __device__ __forceinline__ int seq_len(const DecodeArgs& a, int b) {
-  const int L = a.context_lens[b];
+  const int L = constant_view(a.context_lens)[b];
   return max(0, min(L, a.max_blocks_per_seq * kBlock));
 }
 __device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int b) {
@@ -318,7 +315,7 @@ __device__ __forceinline__ ScanResult scan_blocks(const DecodeArgs& a, int b, in
     const int bb = c0 + lane;
     const int n = bb < a.B ? seq_blocks(a, bb) : 0;
     const int incl = wave_incl_scan(n, lane);
-    const int chunk_total = __shfl(incl, kWave - 1);
+    const int chunk_total = uniform(__shfl(incl, kWave - 1));
     if (b >= c0 && b < c0 + kWave) r.before = r.total + __shfl(incl, b - c0) - __shfl(n, b - c0);
     r.total += chunk_total;
   }
@@ -455,7 +452,7 @@ __device__ __forceinline__ Piece next_piece(const DecodeArgs& a, int HC, const P
 // query registers and first table entry are requested when a piece starts, and
 // its first block is loaded before the current piece's epilogue, whose
 // reductions and stores then hide that load.  Table entries are read with
-// scalar loads one block ahead, so they never hold up the vector loads.
+// scalar loads two blocks ahead, so they never hold up the vector loads.
 template <typename T, int D, int GC>
 struct RangeStream {
   using Sh = DecodeShape<T, D>;
@@ -478,8 +475,10 @@ struct RangeStream {
     return c;
   }
 
-  __device__ static int table_entry(const DecodeArgs& a, const Ctx& c, int j) {
-    const int e = c.trow[j];
+  // Raw table entry (a scalar load); clamped only where it is used, so that the
+  // load has a whole block step to land.
+  __device__ static int table_entry(const Ctx& c, int j) { return constant_view(c.trow)[j]; }
+  __device__ static int clamp_block(const DecodeArgs& a, int e) {
     return (e >= 0 && e < a.n_blocks) ? e : 0;
   }
 
@@ -549,16 +548,27 @@ struct RangeStream {
     const uint4* kc4 = reinterpret_cast<const uint4*>(a.k_cache);
     const uint4* vc4 = reinterpret_cast<const uint4*>(a.v_cache);
     const size_t head_vecs = (size_t)kBlock * Sh::kRowVec;
+    auto block_base = [&](int raw_entry, int kvh) {
+      return ((size_t)clamp_block(a, raw_entry) * a.h_kv + kvh) * head_vecs;
+    };
 
     Ctx cc = ctx_of(a, cur);
     QRegs<GC, VPL> q, qn;
     load_q(a, cur, cc, sub, q);
+    int t = cur.j0;
+    // Table entries are requested two blocks (and, for the next piece, one
+    // piece) ahead of their use: the entry of block t + 1 is in ent[0] at even
+    // steps of the inner loop and in ent[1] at odd steps, so each scalar load
+    // has two block steps to land and is never copied before use.
+    int ent0 = table_entry(cc, min(t + 1, cur.j1 - 1));
+    int ent1 = table_entry(cc, min(t + 2, cur.j1 - 1));
     Piece nxt = next_piece(a, HC, cur, e);
     Ctx nc = nxt.valid ? ctx_of(a, nxt) : cc;
-    int nxt_blk = 0;
+    int nxt_blk0 = 0, nxt_blk1 = 0;
     if (nxt.valid) {
       load_q(a, nxt, nc, sub, qn);
-      nxt_blk = table_entry(a, nc, 0);
+      nxt_blk0 = table_entry(nc, 0);
+      nxt_blk1 = table_entry(nc, min(1, nxt.j1 - 1));
     }
 
     float m[GC], l[GC], acc[GC][EPL];
@@ -573,60 +583,55 @@ struct RangeStream {
     };
     reset();
 
-    int t = cur.j0;
-    int blk_next = cur.j0 + 1 < cur.j1 ? table_entry(a, cc, cur.j0 + 1) : 0;  // one block ahead
     BlockOf<T, D> A, B;
     {
-      const size_t base = ((size_t)table_entry(a, cc, cur.j0) * a.h_kv + cc.kvh) * head_vecs;
+      const size_t base = block_base(table_entry(cc, t), cc.kvh);
       load_block<T, D>(A, kc4 + base, vc4 + base, slot_id, sub);
     }
 
-    // Attends block t (in X) after loading the following block into Y: the
-    // next block of this piece, else the next piece's first block, else a
-    // cache-resident dummy (so that the loop's loads are unconditional).
-    // Returns true when block t was the piece's last.
-    auto step = [&](BlockOf<T, D>& X, BlockOf<T, D>& Y) -> bool {
-      const bool more = t + 1 < cur.j1;
-      int blk, kvh, sl = slot_id, sb = sub;
-      if (more) {
-        blk = blk_next;
-        kvh = cc.kvh;
-      } else if (nxt.valid) {
-        blk = nxt_blk;
-        kvh = nc.kvh;
-      } else {
-        blk = 0;
-        kvh = 0;
-        sl = 0;
-        sb = 0;
+    // Block t (in X) is not the piece's last: load block t + 1 (entry in E)
+    // into Y, request the entry of block t + 3 into E, then attend block t.
+    // A block before the last is always full.
+    auto step_in = [&](BlockOf<T, D>& X, BlockOf<T, D>& Y, int& E) {
+      const size_t base = block_base(E, cc.kvh);
+      load_block<T, D>(Y, kc4 + base, vc4 + base, slot_id, sub);
+      E = table_entry(cc, min(t + 3, cur.j1 - 1));
+      attend_block<T, D, GC, false>(X, q, m, l, acc, a.scale_log2, slot_id, kBlock);
+      ++t;
+    };
+    // Block t (in X) is the piece's last: load the next piece's first block
+    // into Y, if there is a next piece, then attend block t, masking the tokens
+    // past the context.
+    auto step_last = [&](BlockOf<T, D>& X, BlockOf<T, D>& Y) {
+      if (nxt.valid) {
+        const size_t base = block_base(nxt_blk0, nc.kvh);
+        load_block<T, D>(Y, kc4 + base, vc4 + base, slot_id, sub);
       }
-      const size_t base = ((size_t)blk * a.h_kv + kvh) * head_vecs;
-      load_block<T, D>(Y, kc4 + base, vc4 + base, sl, sb);
-      if (t + 2 < cur.j1) blk_next = table_entry(a, cc, t + 2);
       const int valid = cc.L - t * kBlock;
       if (valid >= kBlock)
         attend_block<T, D, GC, false>(X, q, m, l, acc, a.scale_log2, slot_id, kBlock);
       else
         attend_block<T, D, GC, true>(X, q, m, l, acc, a.scale_log2, slot_id, valid);
-      if (more) ++t;
-      return !more;
     };
 
     while (true) {
-      bool in_b;
-      while (true) {
-        if (step(A, B)) {
-          in_b = true;
-          break;
-        }
-        if (step(B, A)) {
-          in_b = false;
-          break;
-        }
+      // Invariant: block t of the current piece is in A (possibly in flight).
+      while (t + 2 < cur.j1) {
+        step_in(A, B, ent0);
+        step_in(B, A, ent1);
+      }
+      bool next_in_b;
+      if (t + 1 < cur.j1) {
+        step_in(A, B, ent0);
+        step_last(B, A);
+        next_in_b = false;
+      } else {
+        step_last(A, B);
+        next_in_b = true;
       }
       epilogue(a, line, W, cur, cc, lane, m, l, acc);
       if (!nxt.valid) break;
-      if (in_b) A = B;  // after the epilogue, so that the load has had time to land
+      if (next_in_b) A = B;  // after the epilogue, so that the load has had time to land
       cur = nxt;
       cc = nc;
 #pragma unroll
@@ -635,12 +640,14 @@ struct RangeStream {
         for (int x = 0; x < VPL * 4; ++x) q.w[j][x] = qn.w[j][x];
       reset();
       t = 0;
-      blk_next = cur.j1 > 1 ? table_entry(a, cc, 1) : 0;
+      ent0 = nxt_blk1;
+      ent1 = table_entry(cc, min(2, cur.j1 - 1));
       nxt = next_piece(a, HC, cur, e);
       if (nxt.valid) {
         nc = ctx_of(a, nxt);
         load_q(a, nxt, nc, sub, qn);
-        nxt_blk = table_entry(a, nc, 0);
+        nxt_blk0 = table_entry(nc, 0);
+        nxt_blk1 = table_entry(nc, min(1, nxt.j1 - 1));
       }
     }
   }
@@ -688,6 +695,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       }
       base += __shfl(incl, kWave - 1);
     }
+    b = uniform(b);
+    nb = uniform(nb);
+    seq0 = uniform(seq0);
     const int64_t r = s - seq0;
     first.b = b;
     first.nb = nb;

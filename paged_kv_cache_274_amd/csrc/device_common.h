@@ -27,16 +27,14 @@ __device__ __forceinline__ float bf16hi_to_f32(uint32_t packed) {
   return __uint_as_float(packed & 0xffff0000u);
 }
 
-// fp32 -> bf16 with round-to-nearest-even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
+// fp32 -> bf16 with round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32); NaN
+// stays NaN.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // Lane permutations inside a row of 16 lanes through DPP (no LDS traffic).
@@ -122,5 +120,25 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wave-uniform copies of values the compiler cannot prove uniform (results of
+// cross-lane shuffles), so that branches on them stay scalar.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+  const uint64_t u = (uint64_t)x;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Read-only metadata (block tables, context lengths) viewed through the
+// constant address space: with a wave-uniform index the load is a scalar
+// load, counted apart from the vector loads of K and V, so waiting for it
+// never waits for K/V data in flight.
+#define PKV_CONSTANT __attribute__((address_space(4)))
+template <typename T>
+__device__ __forceinline__ const PKV_CONSTANT T* constant_view(const T* p) {
+  return (const PKV_CONSTANT T*)p;
+}
 
 }  // namespace pkv

@@ -12,15 +12,27 @@
 //    adjacent rows (row r = token * g + head-in-group), so one K/V tile in LDS
 //    serves the whole group.  A workgroup of 4 wavefronts owns 128 packed rows;
 //    each wavefront owns 32 of them.
-//  * Keys are walked in tiles of 32 (two blocks), gathered through the block
-//    table into LDS: K row-major, V transposed, keys past the context zeroed.
+//  * Keys are walked in tiles of 64 (four blocks).  Each wavefront copies one
+//    block of K and of V per tile straight from HBM into LDS
+//    (global_load_lds_dwordx4, no register staging), and three tile buffers
+//    keep the next two tiles in flight while the current one is used.
+//  * LDS rows are key-major and unpadded; the 16-byte chunk c of row r sits at
+//    chunk position c ^ swz(r), chosen so that both the K operand reads (16
+//    consecutive rows at one chunk) and the transposed V reads (4 rows x 64
+//    bytes) touch every bank once.
 //  * The wavefront computes S^T = K . Q^T (keys x its 32 query rows), so a lane
-//    holds 16 scores of one query column; the row max and sum need only one
-//    exchange with the other half-wave.  The scores' accumulator layout is
-//    exactly the B operand layout of the next product, O^T = V^T . P^T, once
-//    the V^T operand is read with the matching key order.
+//    holds the scores of one query row; the row max and sum need one exchange
+//    with the other half-wave.  The scores' accumulator layout is exactly the B
+//    operand layout of the next product, O^T = V^T . P^T, with the keys of each
+//    16-key chunk taken in the matching order; the V^T operand comes from the
+//    key-major V rows through ds_read_b64_tr_b16, which hands each lane four
+//    consecutive keys of one channel.
 //  * Key tiles past the wavefront's last query position are skipped; only
-//    tiles that cross the diagonal are masked.
+//    tiles that cross the diagonal are masked.  V rows past the context (the
+//    tail of the last block, or blocks beyond it) are zeroed in LDS so that
+//    whatever the pool holds there never reaches the product.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -28,27 +40,80 @@ namespace pkv {
 
 constexpr int kPfWaves = 4;
 constexpr int kPfRows = 32 * kPfWaves;  // packed rows per workgroup
-constexpr int kPfKeys = 32;             // keys per tile
+constexpr int kPfTile = 64;             // keys per tile
 constexpr float kPfNegInf = -__builtin_huge_valf();
+constexpr float kPfSlack = 8.0f;  // log2 units
+
+#define PKV_LDS __attribute__((address_space(3)))
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
-struct PfLds {
-  static constexpr int kKStride = D + 8;        // bf16 elements per K row (16-byte pad)
-  static constexpr int kVStride = kPfKeys + 4;  // bf16 elements per V^T row (8-byte pad)
-  uint16_t k[kPfKeys * kKStride];
-  uint16_t vt[D * kVStride];
+struct PfTile {
+  static constexpr int kChunks = D / 8;              // 16-byte chunks per key row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kMatBytes = kPfTile * kRowBytes;  // K (or V) of one tile
+  static constexpr int kBufBytes = 2 * kMatBytes;
+  static constexpr int kRowsPerCopy = 1024 / kRowBytes;   // rows one wave-wide copy fills
+  static constexpr int kCopiesPerBlock = kBlock / kRowsPerCopy;
+  // Chunk swizzle: a permutation of the row's low bits into the chunk index.
+  __device__ static int swz(int r) {
+    if constexpr (D == 64)
+      return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else
+      return ((r & 3) << 2) | ((r >> 2) & 3);
+  }
+  __device__ static int offset(int r, int chunk) { return r * kRowBytes + ((chunk ^ swz(r)) << 4); }
 };
 
 // Accumulator element r of a 32x32 MFMA result in lane (col, half) is row
 // 8 * (r / 4) + 4 * half + r % 4.
 __device__ __forceinline__ int mfma32_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
+// One wave-wide 16-byte-per-lane copy from global memory straight into LDS:
+// lane l's 16 bytes land at lds_addr + 16 * l.  Issued as inline assembly so
+// that the compiler does not track it: it would otherwise wait for every copy
+// in flight before any LDS read it cannot prove disjoint.  Completion is
+// handled explicitly (wait_vm + tile_barrier).  Compiler-generated vmcnt waits
+// stay correct, only stricter, because loads retire in order.
+__device__ __forceinline__ void copy_to_lds(const void* src, const void* lds_dst) {
+  const unsigned lds_addr = (unsigned)(uintptr_t)(const PKV_LDS unsigned char*)lds_dst;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_addr)
+               : "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+// s_waitcnt lgkmcnt(0): this wave's LDS stores are done.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier without a memory fence: the tiles are published by the
+// explicit waits above each call, and nothing else is shared, so the fence of
+// __syncthreads (which would also wait for the tiles still in flight) is not
+// needed.  The empty asm statements keep the compiler from moving LDS accesses
+// across the barrier.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
-  __shared__ PfLds<D> lds;
+  using Tl = PfTile<D>;
+  // Three tile buffers: tile kt lives in buffer kt % 3.
+  __shared__ __attribute__((aligned(16))) unsigned char buf0[Tl::kBufBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char buf1[Tl::kBufBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char buf2[Tl::kBufBytes];
   constexpr int NC = D / 16;   // 16-channel chunks (K dimension of S^T)
   constexpr int NT = D / 32;   // 32-channel tiles of O^T
+  constexpr int kCopies = 2 * Tl::kCopiesPerBlock;  // copies per wave per tile (K and V)
 
+  // Workgroups with the most key tiles (the last rows of a sequence) first.
+  const int bx = gridDim.x - 1 - blockIdx.x;
   const int s = blockIdx.z;
   const int kvh = blockIdx.y;
   const int g = a.g;
@@ -57,7 +122,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
   int L = a.context_lens[s];
   L = max(0, min(L, a.max_blocks_per_seq * kBlock));
   const int rows = n * g;
-  const int r0 = blockIdx.x * kPfRows;
+  const int r0 = bx * kPfRows;
   if (n <= 0 || n > L || r0 >= rows || q0 < 0 || q0 + n > a.T_q) return;
 
   const int tid = threadIdx.x;
@@ -79,21 +144,15 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
   const int wave_pos_lo = first + wave_r0 / g;
   const int wave_pos_hi = first + (min(wave_r0 + 31, rows - 1)) / g;
   const int wg_pos_hi = first + (min(r0 + kPfRows - 1, rows - 1)) / g;
-  const int n_tiles = (wg_pos_hi + kPfKeys) / kPfKeys;
+  const int n_tiles = uniform(wg_pos_hi / kPfTile + 1);
+  const int Lu = uniform(L);
 
-  // Q^T operand (B of S^T = K Q^T): lane (col, half) holds channels
-  // 16c + 8*half .. +8 of its row; rows past the end are zero.
-  bf16x8_t qb[NC];
-  {
-    const uint4* qv = reinterpret_cast<const uint4*>(a.q);
-    const size_t rowv = ((size_t)(q0 + tok) * a.h_q + kvh * g + hh) * (D / 8);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      uint4 x = row_ok ? qv[rowv + 2 * c + half] : make_uint4(0, 0, 0, 0);
-      qb[c] = __builtin_bit_cast(bf16x8_t, x);
-    }
-  }
-
+  bf16x8_t qb[NC];  // filled once the first tiles are in flight
+  // Scores enter the softmax as s * c with c = |scale| * log2(e) > 0; a negative
+  // scale flips the sign bits of Q instead (exact), so that the row maximum of
+  // s * c is c times the maximum of s.
+  const float csc = fabsf(a.scale_log2);
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
   f32x16_t o[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
@@ -102,128 +161,223 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
   float m = kPfNegInf;
   float lsum = 0.f;
 
-  const uint4* kc = reinterpret_cast<const uint4*>(a.k_cache);
-  const uint4* vc = reinterpret_cast<const uint4*>(a.v_cache);
-  const int32_t* tbl = a.block_tables + (size_t)s * a.max_blocks_per_seq;
-  constexpr int kVecPerRow = D / 8;                   // 16-byte vectors per token row
-  constexpr int kTileVecs = kPfKeys * kVecPerRow;     // vectors per K (or V) tile
+  const unsigned char* kc = reinterpret_cast<const unsigned char*>(a.k_cache);
+  const unsigned char* vc = reinterpret_cast<const unsigned char*>(a.v_cache);
+  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  const size_t head_bytes = (size_t)kBlock * Tl::kRowBytes;
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    // Gather the K and V tiles of keys kt*32 .. kt*32+31 into LDS.
-    for (int i = tid; i < kTileVecs; i += blockDim.x) {
-      const int key = i / kVecPerRow;
-      const int cv = i - key * kVecPerRow;
-      const int kpos = kt * kPfKeys + key;
-      uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
-      if (kpos < L) {
-        int blk = tbl[kpos >> 4];
-        blk = (blk >= 0 && blk < a.n_blocks) ? blk : 0;
-        const size_t src = (((size_t)blk * a.h_kv + kvh) * kBlock + (kpos & 15)) * kVecPerRow + cv;
-        kx = kc[src];
-        vx = vc[src];
-      }
-      *reinterpret_cast<uint4*>(&lds.k[key * PfLds<D>::kKStride + cv * 8]) = kx;
-      const uint32_t vw[4] = {vx.x, vx.y, vx.z, vx.w};
+  // Tile kt lives in buffer kt % 3.
+  auto buffer = [&](auto B) -> unsigned char* {
+    if constexpr (decltype(B)::value == 0)
+      return buf0;
+    else if constexpr (decltype(B)::value == 1)
+      return buf1;
+    else
+      return buf2;
+  };
+
+  // Copies block (4 * kt + wave) of tile kt, K and V, into its buffer.  Lane l
+  // of copy i fills LDS row 16 * wave + i * kRowsPerCopy + l / kChunks at chunk
+  // position l % kChunks, i.e. logical chunk (l % kChunks) ^ swz(row).
+  auto issue_tile = [&](auto B, int kt) {
+    // The entry index stays inside the table row but does not wait for the
+    // context length: entries past the context may hold anything, so the block
+    // id is clamped into the pool, and those rows are masked (K) or zeroed (V).
+    const int bi = min(kt * (kPfTile / kBlock) + wave, a.max_blocks_per_seq - 1);
+    int blk = constant_view(trow)[bi];
+    blk = (blk >= 0 && blk < a.n_blocks) ? blk : 0;
+    const size_t gbase = ((size_t)blk * a.h_kv + kvh) * head_bytes;
+    unsigned char* buf = buffer(B);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lds.vt[(cv * 8 + 2 * e) * PfLds<D>::kVStride + key] = (uint16_t)(vw[e] & 0xffffu);
-        lds.vt[(cv * 8 + 2 * e + 1) * PfLds<D>::kVStride + key] = (uint16_t)(vw[e] >> 16);
-      }
+    for (int i = 0; i < Tl::kCopiesPerBlock; ++i) {
+      const int rb = i * Tl::kRowsPerCopy + lane / Tl::kChunks;       // row within the block
+      const int row = wave * kBlock + rb;                               // row within the tile
+      const int chunk = (lane % Tl::kChunks) ^ Tl::swz(row);
+      const size_t src = gbase + (size_t)rb * Tl::kRowBytes + chunk * 16;
+      const int ldst = (wave * kBlock + i * Tl::kRowsPerCopy) * Tl::kRowBytes;
+      copy_to_lds(kc + src, buf + ldst);
+      copy_to_lds(vc + src, buf + Tl::kMatBytes + ldst);
     }
-    __syncthreads();
+  };
 
-    if (wave_live && kt * kPfKeys <= wave_pos_hi) {
-      // S^T tile: rows = 32 keys, columns = this wave's 32 query rows.
-      f32x16_t st;
+  // Transposed-read addressing: within each 16-lane group, lane j points at key
+  // kq + j / 4 and channel cq + 4 * (j % 4) and receives, for k = 0..3, channel
+  // cq + j of key kq + k.
+  const int grp = lane >> 4;
+  const int tr_row = 4 * (grp >> 1) + ((lane & 15) >> 2);
+  const int tr_ch = 16 * (grp & 1) + 4 * (lane & 3);
+
+  // Attends tile kt (in buffer B): S^T, online softmax, O^T += V^T P^T.
+  auto attend_tile = [&](auto B, int kt) {
+    const unsigned char* kb_lds = buffer(B);
+    const unsigned char* vb_lds = buffer(B) + Tl::kMatBytes;
+    const int key0 = kt * kPfTile;
+    f32x16_t st[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) st[i] = 0.f;
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[h2][i] = 0.f;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint4 kx = *reinterpret_cast<const uint4*>(
-            &lds.k[col * PfLds<D>::kKStride + c * 16 + half * 8]);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx), qb[c], st, 0, 0, 0);
+        const uint4 kx = *reinterpret_cast<const uint4*>(kb_lds + Tl::offset(32 * h2 + col, 2 * c + half));
+        st[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx), qb[c],
+                                                         st[h2], 0, 0, 0);
       }
-      float sv[16];
-      const bool diag = kt * kPfKeys + kPfKeys - 1 > wave_pos_lo;
+    }
+    // Causal mask on tiles that cross the diagonal: element (h2, i) holds key
+    // key0 + 32 * h2 + mfma32_row(i, half), masked when past this row's position;
+    // compared as a compile-time offset against one per-lane limit.
+    if (key0 + kPfTile - 1 > wave_pos_lo) {
+      const int lim = pos - key0 - 4 * half;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = st[i] * a.scale_log2;
-        if (diag && kt * kPfKeys + mfma32_row(i, half) > pos) x = kPfNegInf;
-        sv[i] = x;
-      }
-      float tmax = sv[0];
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, sv[i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mn = fmaxf(m, tmax);
+        for (int i = 0; i < 16; ++i)
+          if (32 * h2 + mfma32_row(i, 0) > lim) st[h2][i] = kPfNegInf;
+    }
+    float tmax = kPfNegInf;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, st[h2][i]);
+    tmax = xor32_max(tmax) * csc;
+    // Lazy rescale: the reference max only moves when a score exceeds it by
+    // more than 2^kPfSlack, so O^T and the sum are rarely rescaled (exact
+    // either way: the weights are taken against the same reference m).
+    if (__any(tmax > m + kPfSlack)) {
+      const float mn = tmax > m + kPfSlack ? tmax : m;
       const float alpha = mn == m ? 1.f : fast_exp2(m - mn);
       m = mn;
-      float p[16];
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = fast_exp2(sv[i] - mn);
-        ps += p[i];
-      }
-      lsum = lsum * alpha + ps;
+      lsum *= alpha;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-
-      // P^T operand for key chunk c (keys 16c..16c+15): element e of lane
-      // (col, half) is key 16c + 8*(e/4) + 4*half + e%4 = accumulator 8c + e.
+    }
+    const float mn = m;
+    float ps = 0.f;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        uint4 pw;
-        pw.x = pack_bf16x2(p[8 * c + 0], p[8 * c + 1]);
-        pw.y = pack_bf16x2(p[8 * c + 2], p[8 * c + 3]);
-        pw.z = pack_bf16x2(p[8 * c + 4], p[8 * c + 5]);
-        pw.w = pack_bf16x2(p[8 * c + 6], p[8 * c + 7]);
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          // V^T operand: row = channel 32t + col, same key order as P^T.
-          const uint16_t* vrow = &lds.vt[(t * 32 + col) * PfLds<D>::kVStride + 16 * c + 4 * half];
-          uint4 vx;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-          vx.x = lo.x; vx.y = lo.y; vx.z = hi.x; vx.w = hi.y;
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vx), pb, o[t], 0, 0, 0);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(st[h2][i], csc, -mn));
+        st[h2][i] = p;
+        ps += p;
+      }
+    lsum += ps;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      // P^T operand for keys 16c .. 16c + 15: element e of lane (col, half) is
+      // key 16c + 8 * (e / 4) + 4 * half + e % 4 = accumulator 8 * (c % 2) + e of
+      // half-tile c / 2.
+      const f32x16_t& sc = st[c >> 1];
+      const int e0 = 8 * (c & 1);
+      uint4 pw;
+      pw.x = pack_bf16x2(sc[e0 + 0], sc[e0 + 1]);
+      pw.y = pack_bf16x2(sc[e0 + 2], sc[e0 + 3]);
+      pw.z = pack_bf16x2(sc[e0 + 4], sc[e0 + 5]);
+      pw.w = pack_bf16x2(sc[e0 + 6], sc[e0 + 7]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        // V^T operand: row = channel 32t + col, keys in the order of P^T.
+        const int ch = 32 * t + tr_ch;
+        const int ra = 16 * c + tr_row;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS i16x4_t*)(vb_lds + Tl::offset(ra, ch >> 3) + (ch & 4) * 2));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS i16x4_t*)(vb_lds + Tl::offset(ra + 8, ch >> 3) + (ch & 4) * 2));
+        const i16x4_t lohi[2] = {lo, hi};
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lohi), pb,
+                                                       o[t], 0, 0, 0);
       }
     }
-    __syncthreads();
+  };
+
+  // One step of the tile walk for tile kt in buffer B; false past the last tile.
+  auto step = [&](auto B, int kt) -> bool {
+    if (kt >= n_tiles) return false;
+    // This wave's copies of tile kt have landed once only tile kt + 1's remain;
+    // after the barrier every wave's have, and every wave is done with tile
+    // kt - 1, whose buffer the copy of tile kt + 2 then refills.
+    if (kt + 1 < n_tiles)
+      wait_vm<kCopies>();
+    else
+      wait_vm<0>();
+    tile_barrier();
+    const int key0 = kt * kPfTile;
+    if (key0 + kPfTile > Lu) {
+      // Zero the V rows past the context.
+      unsigned char* vb = buffer(B) + Tl::kMatBytes;
+      const int zr = max(0, Lu - key0);
+      for (int i = tid; i < (kPfTile - zr) * Tl::kChunks; i += 256)
+        *reinterpret_cast<uint4*>(vb + (zr + i / Tl::kChunks) * Tl::kRowBytes + (i % Tl::kChunks) * 16) =
+            make_uint4(0, 0, 0, 0);
+      wait_lds();
+      tile_barrier();
+    }
+    if (kt + 2 < n_tiles) issue_tile(std::integral_constant<int, (decltype(B)::value + 2) % 3>{}, kt + 2);
+    if (wave_live && key0 <= wave_pos_hi) attend_tile(B, kt);
+    return true;
+  };
+
+  issue_tile(std::integral_constant<int, 0>{}, 0);
+  if (n_tiles > 1) issue_tile(std::integral_constant<int, 1>{}, 1);
+
+  // Q^T operand (B of S^T = K Q^T): lane (col, half) holds channels
+  // 16c + 8*half .. +8 of its row; rows past the end are zero.  The wait that
+  // follows also covers the first two tiles' copies, issued just before, so
+  // no load is left pending that the loop below would wait on.
+  {
+    const uint4* qv = reinterpret_cast<const uint4*>(a.q);
+    const size_t rowv = ((size_t)(q0 + tok) * a.h_q + kvh * g + hh) * (D / 8);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint4 x = row_ok ? qv[rowv + 2 * c + half] : make_uint4(0, 0, 0, 0);
+      x.x ^= qsign;
+      x.y ^= qsign;
+      x.z ^= qsign;
+      x.w ^= qsign;
+      qb[c] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+  wait_vm<0>();
+  for (int kt = 0;; kt += 3) {
+    if (!step(std::integral_constant<int, 0>{}, kt)) break;
+    if (!step(std::integral_constant<int, 1>{}, kt + 1)) break;
+    if (!step(std::integral_constant<int, 2>{}, kt + 2)) break;
   }
 
   if (!row_ok) return;
-  const float lt = lsum + __shfl_xor(lsum, 32);
+  const float lt = xor32_sum(lsum);
   const float inv = 1.f / lt;
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
   const size_t orow = ((size_t)(q0 + tok) * a.h_q + kvh * g + hh) * D;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const int ch = t * 32 + 8 * grp + 4 * half;
+    for (int gq = 0; gq < 4; ++gq) {
+      const int ch = t * 32 + 8 * gq + 4 * half;
       uint2 w;
-      w.x = pack_bf16x2(o[t][4 * grp + 0] * inv, o[t][4 * grp + 1] * inv);
-      w.y = pack_bf16x2(o[t][4 * grp + 2] * inv, o[t][4 * grp + 3] * inv);
+      w.x = pack_bf16x2(o[t][4 * gq + 0] * inv, o[t][4 * gq + 1] * inv);
+      w.y = pack_bf16x2(o[t][4 * gq + 2] * inv, o[t][4 * gq + 3] * inv);
       *reinterpret_cast<uint2*>(&out[orow + ch]) = w;
     }
 }
 
-hipError_t launch_prefill_bf16(const PrefillArgs& a, int d_h, hipStream_t stream) {
+template <int D>
+static hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.max_q_len * a.g;
   const int64_t gx = (rows + kPfRows - 1) / kPfRows;
-  dim3 grid((unsigned)gx, a.h_kv, a.S);
-  if (d_h == 64)
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(256), 0, stream, a);
-  else if (d_h == 128)
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(256), 0, stream, a);
-  else
-    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)gx, a.h_kv, a.S), dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int d_h, hipStream_t stream) {
+  if (d_h == 64) return launch_d<64>(a, stream);
+  if (d_h == 128) return launch_d<128>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv

@@ -101,13 +101,14 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
+// KS wave groups of 4 share a workgroup's 128 rows and split its key tiles:
+// group G takes tiles G, G + KS, G + 2 KS, ... with three buffers of its own,
+// and the groups' softmax states are merged at the end.  KS = 2 halves the
+// serial key walk of the longest rows when the grid alone cannot fill the chip.
+template <int D, int KS>
+__global__ __launch_bounds__(256 * KS) void prefill_bf16_kernel(PrefillArgs a) {
   using Tl = PfTile<D>;
-  // Three tile buffers: tile kt lives in buffer kt % 3.
-  __shared__ __attribute__((aligned(16))) unsigned char buf0[Tl::kBufBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char buf1[Tl::kBufBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char buf2[Tl::kBufBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[KS * 3 * Tl::kBufBytes];
   constexpr int NC = D / 16;   // 16-channel chunks (K dimension of S^T)
   constexpr int NT = D / 32;   // 32-channel tiles of O^T
   constexpr int kCopies = 2 * Tl::kCopiesPerBlock;  // copies per wave per tile (K and V)
@@ -127,7 +128,8 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // row wave in the group
+  const int grp_id = __builtin_amdgcn_readfirstlane(tid >> 8);       // key-split group
   const int col = lane & 31;
   const int half = lane >> 5;
   const int first = L - n;  // position of query 0
@@ -145,6 +147,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
   const int wave_pos_hi = first + (min(wave_r0 + 31, rows - 1)) / g;
   const int wg_pos_hi = first + (min(r0 + kPfRows - 1, rows - 1)) / g;
   const int n_tiles = uniform(wg_pos_hi / kPfTile + 1);
+  const int n_steps = (n_tiles + KS - 1) / KS;  // tiles per group, rounded up
   const int Lu = uniform(L);
 
   bf16x8_t qb[NC];  // filled once the first tiles are in flight
@@ -166,15 +169,11 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
   const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   const size_t head_bytes = (size_t)kBlock * Tl::kRowBytes;
 
-  // Tile kt lives in buffer kt % 3.
-  auto buffer = [&](auto B) -> unsigned char* {
-    if constexpr (decltype(B)::value == 0)
-      return buf0;
-    else if constexpr (decltype(B)::value == 1)
-      return buf1;
-    else
-      return buf2;
+  // The group's i-th tile lives in its buffer i % 3.
+  auto buffer_of = [&](int group, auto B) -> unsigned char* {
+    return lds + (group * 3 + decltype(B)::value) * Tl::kBufBytes;
   };
+  auto buffer = [&](auto B) -> unsigned char* { return buffer_of(grp_id, B); };
 
   // Copies block (4 * kt + wave) of tile kt, K and V, into its buffer.  Lane l
   // of copy i fills LDS row 16 * wave + i * kRowsPerCopy + l / kChunks at chunk
@@ -294,35 +293,41 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
     }
   };
 
-  // One step of the tile walk for tile kt in buffer B; false past the last tile.
-  auto step = [&](auto B, int kt) -> bool {
-    if (kt >= n_tiles) return false;
-    // This wave's copies of tile kt have landed once only tile kt + 1's remain;
-    // after the barrier every wave's have, and every wave is done with tile
-    // kt - 1, whose buffer the copy of tile kt + 2 then refills.
-    if (kt + 1 < n_tiles)
+  // Step i of the walk: every group attends its i-th tile, tile kt = i * KS +
+  // group, from buffer B = i % 3; false past the last step.  All groups pass
+  // the same barriers.
+  auto step = [&](auto B, int i) -> bool {
+    if (i >= n_steps) return false;
+    const int kt = i * KS + grp_id;
+    const bool mine = kt < n_tiles;
+    // This wave's copies of tile kt have landed once only the group's next
+    // tile's remain; after the barrier every wave's have, and every wave is
+    // done with its previous tile, whose buffer the copy two tiles ahead then
+    // refills.
+    if (mine && kt + KS < n_tiles)
       wait_vm<kCopies>();
     else
       wait_vm<0>();
     tile_barrier();
-    const int key0 = kt * kPfTile;
-    if (key0 + kPfTile > Lu) {
-      // Zero the V rows past the context.
-      unsigned char* vb = buffer(B) + Tl::kMatBytes;
-      const int zr = max(0, Lu - key0);
-      for (int i = tid; i < (kPfTile - zr) * Tl::kChunks; i += 256)
-        *reinterpret_cast<uint4*>(vb + (zr + i / Tl::kChunks) * Tl::kRowBytes + (i % Tl::kChunks) * 16) =
+    const int last = n_tiles - 1;  // the only tile that can reach past the context
+    if (i == last / KS && (last + 1) * kPfTile > Lu) {
+      // Zero its V rows past the context (all threads, in the owning group's buffer).
+      unsigned char* vb = buffer_of(last % KS, B) + Tl::kMatBytes;
+      const int zr = max(0, Lu - last * kPfTile);
+      for (int z = tid; z < (kPfTile - zr) * Tl::kChunks; z += 256 * KS)
+        *reinterpret_cast<uint4*>(vb + (zr + z / Tl::kChunks) * Tl::kRowBytes + (z % Tl::kChunks) * 16) =
             make_uint4(0, 0, 0, 0);
       wait_lds();
       tile_barrier();
     }
-    if (kt + 2 < n_tiles) issue_tile(std::integral_constant<int, (decltype(B)::value + 2) % 3>{}, kt + 2);
-    if (wave_live && key0 <= wave_pos_hi) attend_tile(B, kt);
+    if (mine && kt + 2 * KS < n_tiles)
+      issue_tile(std::integral_constant<int, (decltype(B)::value + 2) % 3>{}, kt + 2 * KS);
+    if (mine && wave_live && kt * kPfTile <= wave_pos_hi) attend_tile(B, kt);
     return true;
   };
 
-  issue_tile(std::integral_constant<int, 0>{}, 0);
-  if (n_tiles > 1) issue_tile(std::integral_constant<int, 1>{}, 1);
+  if (grp_id < n_tiles) issue_tile(std::integral_constant<int, 0>{}, grp_id);
+  if (grp_id + KS < n_tiles) issue_tile(std::integral_constant<int, 1>{}, grp_id + KS);
 
   // Q^T operand (B of S^T = K Q^T): lane (col, half) holds channels
   // 16c + 8*half .. +8 of its row; rows past the end are zero.  The wait that
@@ -342,10 +347,41 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
     }
   }
   wait_vm<0>();
-  for (int kt = 0;; kt += 3) {
-    if (!step(std::integral_constant<int, 0>{}, kt)) break;
-    if (!step(std::integral_constant<int, 1>{}, kt + 1)) break;
-    if (!step(std::integral_constant<int, 2>{}, kt + 2)) break;
+  for (int i = 0;; i += 3) {
+    if (!step(std::integral_constant<int, 0>{}, i)) break;
+    if (!step(std::integral_constant<int, 1>{}, i + 1)) break;
+    if (!step(std::integral_constant<int, 2>{}, i + 2)) break;
+  }
+
+  if constexpr (KS == 2) {
+    // Group 1 hands its state for the same rows to group 0 through LDS (field
+    // f of lane l of row wave w at float (f * 4 + w) * 64 + l), which merges
+    // the two with the log-sum-exp rule.
+    constexpr int kFields = NT * 16 + 2;
+    static_assert(kFields * 4 * 64 * 4 <= (int)sizeof(lds), "merge area");
+    float* mg = reinterpret_cast<float*>(lds);
+    auto at = [&](int f) -> float& { return mg[(f * 4 + wave) * 64 + lane]; };
+    tile_barrier();  // every wave is done with the tile buffers
+    if (grp_id == 1) {
+      at(0) = m;
+      at(1) = lsum;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) at(2 + t * 16 + e) = o[t][e];
+    }
+    wait_lds();
+    tile_barrier();
+    if (grp_id == 1) return;
+    const float m1 = at(0);
+    const float mm = fmaxf(m, m1);
+    const float a0 = fast_exp2(m - mm);
+    const float a1 = m1 == kPfNegInf ? 0.f : fast_exp2(m1 - mm);
+    lsum = lsum * a0 + at(1) * a1;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[t][e] = o[t][e] * a0 + at(2 + t * 16 + e) * a1;
   }
 
   if (!row_ok) return;
@@ -365,12 +401,32 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
     }
 }
 
+static int compute_units() {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    return n;
+  }();
+  return cus;
+}
+
 template <int D>
 static hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.max_q_len * a.g;
   const int64_t gx = (rows + kPfRows - 1) / kPfRows;
-  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)gx, a.h_kv, a.S), dim3(256), 0,
-                     stream, a);
+  const dim3 grid((unsigned)gx, a.h_kv, a.S);
+  // Split the key walk over two wave groups when the grid has no more
+  // workgroups than the chip has compute units (d_h = 64: eight waves of this
+  // kernel fit one compute unit's registers).
+  if constexpr (D == 64) {
+    if (gx * a.h_kv * a.S <= compute_units()) {
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, 2>), grid, dim3(512), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, 1>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

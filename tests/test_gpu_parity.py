@@ -191,6 +191,9 @@ PREFILL_GRID = [
     (128, 8, 1, [(150, 150), (260, 130)]),
     (64, 16, 2, [(1000, 200), (48, 48)]),
     (128, 6, 3, [(70, 70), (33, 2)]),
+    # many 64-key tiles, ragged context tails, chunks that start mid-tile
+    (128, 32, 8, [(3000, 700), (2049, 2049)]),
+    (64, 14, 2, [(4096, 64), (777, 777), (1, 1)]),
 ]
 
 
@@ -201,6 +204,19 @@ def test_prefill_grid(d, h_q, h_kv, seqs):
                 free_frac=0.2, poison=True)
     res = run(w, DEV)
     kc_ref, vc_ref = check_append(w, res)
+    check_prefill(w, res, kc_ref, vc_ref)
+
+
+@pytest.mark.parametrize("scale", [-0.2, 1.0])
+def test_negative_and_large_scale(scale):
+    """Any finite scale: a negative one reverses the ranking of the keys, a
+    large one makes the softmax nearly one-hot (decode and prefill)."""
+    rng = np.random.default_rng(77)
+    w = W.build("scale", rng, dtype="bf16", h_q=8, h_kv=2, d=128, decode_lens=[300, 17, 1000],
+                prefill=[(257, 100), (64, 64)], free_frac=0.2, poison=True, scale=scale)
+    res = run(w, DEV)
+    kc_ref, vc_ref = check_append(w, res)
+    check_decode(w, res, kc_ref, vc_ref)
     check_prefill(w, res, kc_ref, vc_ref)
 
 

@@ -15,8 +15,9 @@ with wall clock between two synchronisations.
 Printed as one JSON line:
   value      KV bytes attended per second (GB/s), whole step (append + decode)
   roofline   the decode call (its two kernels; HIP events on the launch stream
-             around K back-to-back calls after the timed steps, and around each
-             call inside the steps) against the 8 TB/s HBM peak; algorithmic bytes per
+             around K back-to-back calls after the timed steps; in_step_* from
+             events around each call of K more steps) against the 8 TB/s HBM
+             peak; algorithmic bytes per
              call = sum_b L_b * 2 * h_kv * d_h * 2 B (the KV-cache footprint
              per token of one layer: LLM Inference Server page, Required
              Mathematical Concepts); traffic = counter-measured HBM bytes per
@@ -139,14 +140,24 @@ class Resident:
                                     self.w.pre_max_q_len, scale=self.w.scale, out=self.pre_out)
 
 
-def time_decode_step(r: Resident, steps: int, warmup: int):
+def time_steps(r: Resident, steps: int, warmup: int) -> float:
+    """Wall time of `steps` whole steps (append + decode), nothing else queued."""
     for i in range(warmup):
         r.append(i)
         r.decode(i)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        r.append(i)
+        r.decode(i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def time_step_parts(r: Resident, steps: int):
+    """Per-call HIP-event durations of the append and the decode inside steps."""
     mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     ev = [(mk(), mk(), mk()) for _ in range(steps)]
-    t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record()
         r.append(i)
@@ -154,10 +165,9 @@ def time_decode_step(r: Resident, steps: int, warmup: int):
         r.decode(i)
         ev[i][2].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     app_ms = [a.elapsed_time(b) for a, b, _ in ev]
     dec_ms = [b.elapsed_time(c) for _, b, c in ev]
-    return wall, app_ms, dec_ms
+    return app_ms, dec_ms
 
 
 def time_decode_calls(r: Resident, iters: int, warmup: int = 3):
@@ -473,10 +483,11 @@ def main(argv=None):
 
     wk = W.config(args.config)
     rk = Resident(wk, dev, copies=args.copies)
-    wall, app_ms, dec_ms = time_decode_step(rk, args.steps, args.warmup)
+    wall = time_steps(rk, args.steps, args.warmup)
     kvb = kv_bytes(wk)
     value = kvb * args.steps / wall / 1e9
     dec_avg_s = time_decode_calls(rk, args.steps) / 1e3
+    app_ms, dec_ms = time_step_parts(rk, args.steps)
     achieved = kvb / dec_avg_s / 1e9
     app_bytes = 2 * wk.T * wk.h_kv * wk.d * wk.elem_bytes * 2 + wk.T * 8
     del rk

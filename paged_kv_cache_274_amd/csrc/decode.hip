@@ -614,24 +614,40 @@ struct RangeStream {
         attend_block<T, D, GC, true>(X, q, m, l, acc, a.scale_log2, slot_id, valid);
     };
 
+    // Block t of the current piece is in A, or in B when in_b (a register copy
+    // from B to A would wait for that block's loads and drain the pipeline, so
+    // the roles swap instead: one step from B realigns the walk to A).
+    bool in_b = false;
     while (true) {
-      // Invariant: block t of the current piece is in A (possibly in flight).
-      while (t + 2 < cur.j1) {
-        step_in(A, B, ent0);
-        step_in(B, A, ent1);
+      bool ended = false;
+      if (in_b) {
+        if (t + 1 < cur.j1) {
+          step_in(B, A, ent0);
+          const int e = ent0;
+          ent0 = ent1;
+          ent1 = e;
+        } else {
+          step_last(B, A);
+          ended = true;
+          in_b = false;
+        }
       }
-      bool next_in_b;
-      if (t + 1 < cur.j1) {
-        step_in(A, B, ent0);
-        step_last(B, A);
-        next_in_b = false;
-      } else {
-        step_last(A, B);
-        next_in_b = true;
+      if (!ended) {
+        while (t + 2 < cur.j1) {
+          step_in(A, B, ent0);
+          step_in(B, A, ent1);
+        }
+        if (t + 1 < cur.j1) {
+          step_in(A, B, ent0);
+          step_last(B, A);
+          in_b = false;
+        } else {
+          step_last(A, B);
+          in_b = true;
+        }
       }
       epilogue(a, line, W, cur, cc, lane, m, l, acc);
       if (!nxt.valid) break;
-      if (next_in_b) A = B;  // after the epilogue, so that the load has had time to land
       cur = nxt;
       cc = nc;
 #pragma unroll

@@ -14,25 +14,32 @@
 
 namespace pkv {
 
+// I is the index type: 32-bit when every vector index fits, which keeps the
+// division by the row count short.
+template <typename I>
 __global__ __launch_bounds__(256) void kv_append_kernel(
     const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
     const int64_t* __restrict__ slot_mapping, uint4* __restrict__ k_cache,
-    uint4* __restrict__ v_cache, int64_t total_vecs, int h_kv, int vec_per_row,
-    int64_t n_slots) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint4* __restrict__ v_cache, I total_vecs, int h_kv, int vec_per_row, int64_t n_slots) {
+  const I gid = (I)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total_vecs) return;
-  const int64_t per_token = (int64_t)h_kv * vec_per_row;
-  const int64_t tok = gid / per_token;
+  const I per_token = (I)h_kv * vec_per_row;
+  const I tok = gid / per_token;
   const int rem = (int)(gid - tok * per_token);
   const int head = rem / vec_per_row;
   const int c = rem - head * vec_per_row;
-  const int64_t slot = slot_mapping[tok];
+  // The rows are requested together with the slot, so that the copy waits for
+  // one memory round trip, not two (the empty asm keeps all three loads above
+  // the slot test).
+  int64_t slot = slot_mapping[tok];
+  uint4 kv = k_new[gid];
+  uint4 vv = v_new[gid];
+  asm volatile("" : "+v"(slot), "+v"(kv.x), "+v"(kv.y), "+v"(kv.z), "+v"(kv.w), "+v"(vv.x),
+               "+v"(vv.y), "+v"(vv.z), "+v"(vv.w));
   if (slot < 0 || slot >= n_slots) return;  // padding, or out of range: no write
   const int64_t blk = slot >> 4;
   const int off = (int)(slot & 15);
   const int64_t dst = ((blk * h_kv + head) * kBlock + off) * vec_per_row + c;
-  const uint4 kv = k_new[gid];
-  const uint4 vv = v_new[gid];
   k_cache[dst] = kv;
   v_cache[dst] = vv;
 }
@@ -44,9 +51,16 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t*
   const int64_t total = (int64_t)T * h_kv * vec_per_row;
   const int threads = 256;
   const int64_t grid = (total + threads - 1) / threads;
-  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)grid), dim3(threads), 0, stream,
-                     (const uint4*)k_new, (const uint4*)v_new, slot_mapping, (uint4*)k_cache,
-                     (uint4*)v_cache, total, h_kv, vec_per_row, (int64_t)n_blocks * kBlock);
+  const int64_t n_slots = (int64_t)n_blocks * kBlock;
+  if (total + threads <= INT32_MAX)
+    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, dim3((unsigned)grid), dim3(threads), 0,
+                       stream, (const uint4*)k_new, (const uint4*)v_new, slot_mapping,
+                       (uint4*)k_cache, (uint4*)v_cache, (uint32_t)total, h_kv, vec_per_row,
+                       n_slots);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<int64_t>, dim3((unsigned)grid), dim3(threads), 0,
+                       stream, (const uint4*)k_new, (const uint4*)v_new, slot_mapping,
+                       (uint4*)k_cache, (uint4*)v_cache, total, h_kv, vec_per_row, n_slots);
   return hipGetLastError();
 }
 

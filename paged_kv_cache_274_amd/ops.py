@@ -156,6 +156,17 @@ def paged_prefill_attention(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache
                             scale: Optional[float] = None,
                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Causal chunked prefill over paged K/V.  q, out: packed [T_q, h_q, d_h]."""
+    return bind_prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, max_q_len,
+                        scale, out)()
+
+
+def bind_prefill(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache: torch.Tensor,
+                 v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                 max_q_len: int, scale: Optional[float] = None,
+                 out: Optional[torch.Tensor] = None):
+    """Checks and marshals the arguments of paged_prefill_attention once and
+    returns a call that launches it on them (on the stream current now), for
+    loops that re-run one prefill on the same buffers.  The call returns out."""
     n_blocks, h_kv, d = _pool_shape(k_cache, v_cache)
     _need(q.dim() == 3 and q.shape[2] == d and q.dtype == k_cache.dtype,
           "q must be [T_q, h_q, d_h]")
@@ -172,11 +183,15 @@ def paged_prefill_attention(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache
     _dev(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, out)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    rc = lib().paged_prefill_attention(
-        out.data_ptr(), q.data_ptr(), cu_seqlens_q.data_ptr(), k_cache.data_ptr(),
-        v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), S, T_q,
-        int(max_q_len), h_q, h_kv, d, n_blocks, int(block_tables.shape[1]), float(scale),
-        _DTYPE[q.dtype], _stream(q))
-    if rc != 0:
-        raise PkvError("paged_prefill_attention", rc)
-    return out
+    fn = lib().paged_prefill_attention
+    args = (out.data_ptr(), q.data_ptr(), cu_seqlens_q.data_ptr(), k_cache.data_ptr(),
+            v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), S, T_q,
+            int(max_q_len), h_q, h_kv, d, n_blocks, int(block_tables.shape[1]), float(scale),
+            _DTYPE[q.dtype], _stream(q))
+
+    def call() -> torch.Tensor:
+        rc = fn(*args)
+        if rc != 0:
+            raise PkvError("paged_prefill_attention", rc)
+        return out
+    return call

@@ -115,6 +115,43 @@ def test_decode_split_invariance(splits):
     check_decode(w, res, kc_ref, vc_ref)
 
 
+CURSOR_MIXES = [
+    # name, lens, h_q, h_kv, d
+    ("many short", [int(x) for x in np.random.default_rng(41).integers(1, 40, size=300)], 8, 2, 64),
+    ("zeros between", [0, 500, 0, 0, 17, 3000, 0, 1, 0], 32, 8, 128),
+    ("one long", [30000], 32, 8, 128),
+    ("one long, one head", [20011], 4, 1, 64),
+    ("fewer blocks than groups", [5, 3], 8, 1, 128),
+]
+
+
+@pytest.mark.parametrize("name,lens,h_q,h_kv,d", CURSOR_MIXES, ids=[m[0] for m in CURSOR_MIXES])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_automatic_split_length_mixes(name, lens, h_q, h_kv, d, dtype):
+    """The automatic split on length mixes that stress its bookkeeping: many
+    segments per wave, empty sequences, a segment spread over every wave (more
+    than 64 pieces to merge), and fewer blocks than waves."""
+    rng = np.random.default_rng(sum(lens) % 1000 + h_q)
+    # a decode step appends one token, so the workload has length >= 1; the
+    # zero-length sequences are given to a second decode call directly
+    w = W.build("mix", rng, dtype=dtype, h_q=h_q, h_kv=h_kv, d=d,
+                decode_lens=[max(1, L) for L in lens], free_frac=0.1, poison=True)
+    res = run(w, DEV, num_splits=0)
+    kc_ref, vc_ref = check_append(w, res)
+    check_decode(w, res, kc_ref, vc_ref)
+    if 0 in lens:
+        lz = torch.tensor(lens, dtype=torch.int32)
+        out = ops.paged_decode_attention(w.dec_q.to(DEV), res.k_cache.to(DEV),
+                                         res.v_cache.to(DEV), w.dec_block_tables.to(DEV),
+                                         lz.to(DEV), max(lens), scale=w.scale).cpu()
+        ref = O.decode(pins.np64(w.dec_q), kc_ref, vc_ref, w.dec_block_tables.numpy(),
+                       lz.numpy(), w.scale)
+        assert max_err(out, ref) <= TOL[w.dtype]
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert torch.count_nonzero(out[b]) == 0
+
+
 def _pool_from_logical(Ks, Vs, seed, dtype, extra=5, prefix_share=0):
     kc, vc, t = pins.page(Ks, Vs, np.random.default_rng(seed), extra_blocks=extra,
                           prefix_share=prefix_share)

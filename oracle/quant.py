@@ -1,0 +1,93 @@
+"""CPU oracle for the INT8 KV cache (NumPy).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The
+library (``paged_kv_cache_274_amd``) never does, and this module imports
+nothing from it.
+
+What it computes, in the pages' order and notation:
+
+* The cached K and V are quantised dynamically to int8 per token head (LLM
+  Inference Server page, "INT8 KV-Cache Quantization" stretch challenge): each
+  row of d_h values that one token holds for one KV head gets its own scale.
+
+* The quantiser is the symmetric absmax rule the same page lists under
+  "Required Mathematical Concepts": s = max|x| / 127, x_q = round(x / s),
+  x_hat = s * x_q.  Its printed reference layer ("Starter & Verification Code
+  Examples", the INT8 linear layer) fixes the details followed here: the values
+  are taken in float32, the absolute maximum is floored at 1e-8 before the
+  division (so an all-zero row gets codes 0), the division is a float32
+  division, and ``round`` is PyTorch's, which rounds halves to even.  The
+  codes then lie in [-127, 127].
+
+* Reading where the pages are silent: the printed layer stores its scale in the
+  weight dtype; for the cache the scale is kept as the float32 value computed
+  (s in the formula), one per (block, KV head, slot), beside int8 codes laid out
+  like the bf16 pools.
+
+* Attention over an INT8 cache is attention over the dequantised values
+  x_hat = s * x_q (exact in float64), i.e. ``attention.decode`` applied to the
+  dequantised pools.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import attention as A
+
+QMAX = np.float32(127.0)
+AMAX_FLOOR = np.float32(1e-8)
+
+
+def absmax_scale(row) -> np.float32:
+    """s = max(max|x|, 1e-8) / 127 in float32 (x widened to float32 first)."""
+    x = np.asarray(row, dtype=np.float32)
+    amax = np.float32(np.abs(x).max()) if x.size else np.float32(0.0)
+    return np.float32(np.maximum(amax, AMAX_FLOOR) / QMAX)
+
+
+def quantize_row(row):
+    """(codes int8 [d], s float32): x_q = round_half_even(x / s), float32 division."""
+    x = np.asarray(row, dtype=np.float32)
+    s = absmax_scale(x)
+    codes = np.rint(x / s)
+    return codes.astype(np.int8), s
+
+
+def dequantize(codes, scales) -> np.ndarray:
+    """x_hat = s * x_q in float64 (exact: a float32 times an integer of 8 bits)."""
+    return np.asarray(codes, dtype=np.float64) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def kv_append_int8(k_new, v_new, slot_mapping, k_codes, v_codes, k_scales, v_scales):
+    """Copies of the int8 pools and scale pools with each new token's rows
+    quantised and written at its slot.  Pools: codes [n_blocks, h_kv, 16, d_h]
+    int8, scales [n_blocks, h_kv, 16] float32.  A negative slot means no write;
+    duplicate or out-of-range slots raise ValueError."""
+    kq = np.array(k_codes, copy=True)
+    vq = np.array(v_codes, copy=True)
+    ks = np.array(k_scales, copy=True)
+    vs = np.array(v_scales, copy=True)
+    slots = [int(s) for s in np.asarray(slot_mapping).reshape(-1)]
+    n_slots = kq.shape[0] * A.BLOCK
+    live = [s for s in slots if s >= 0]
+    if len(set(live)) != len(live):
+        raise ValueError("duplicate slot in slot_mapping")
+    if any(s >= n_slots for s in live):
+        raise ValueError("slot outside the pool")
+    h_kv = kq.shape[1]
+    for i, s in enumerate(slots):
+        if s < 0:
+            continue
+        blk, off = A.slot_to_block(s)
+        for h in range(h_kv):
+            kq[blk, h, off], ks[blk, h, off] = quantize_row(k_new[i][h])
+            vq[blk, h, off], vs[blk, h, off] = quantize_row(v_new[i][h])
+    return kq, vq, ks, vs
+
+
+def decode_int8(q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens,
+                scale: float) -> np.ndarray:
+    """Decode attention over the dequantised cache (float64)."""
+    return A.decode(q, dequantize(k_codes, k_scales), dequantize(v_codes, v_scales), block_tables,
+                    context_lens, scale)

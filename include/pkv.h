@@ -54,7 +54,10 @@
 extern "C" {
 #endif
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+/* PKV_INT8 names the INT8 cache (int8 codes with a float32 scale per token
+ * head row, read by bf16 queries); it is accepted by pkv_decode_num_splits and
+ * pkv_decode_workspace_bytes only. */
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_INT8 = 2 } pkv_dtype;
 
 typedef enum {
   PKV_OK = 0,
@@ -127,6 +130,50 @@ int paged_decode_attention(void* out, const void* q,
                            int max_blocks_per_seq, int max_context_len,
                            float scale, int dtype, int num_splits,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * INT8 KV cache.  The cached K and V are quantised dynamically to int8 per
+ * token head (LLM Inference Server page, Optional Stretch Challenges, "INT8
+ * KV-Cache Quantization") with the symmetric absmax rule of the same page
+ * (Required Mathematical Concepts): for each row x of d_h values that one token
+ * holds for one KV head, s = max(max|x|, 1e-8) / 127 and x_q = round(x / s),
+ * computed in float32 with a true division and rounding half to even, as in the
+ * page's reference INT8 layer (Starter & Verification Code Examples).  The
+ * cache holds x_hat = s * x_q.
+ *
+ *   k_cache, v_cache : device int8 [n_blocks, h_kv, 16, d_h] (codes, laid out
+ *                      like the bf16 pools)
+ *   k_scale, v_scale : device float32 [n_blocks, h_kv, 16] (s of each row),
+ *                      4-byte aligned
+ */
+
+/*
+ * kv_append_int8 - quantise the K and V rows of T new tokens and write codes
+ * and scales to their pool slots, in place.  Arguments as for kv_append;
+ * dtype (PKV_F32 or PKV_BF16) is that of k_new and v_new.  The codes and
+ * scales are bit-exact against the rule above.
+ */
+int kv_append_int8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                   int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale,
+                   int T, int h_kv, int d_h, int n_blocks, int dtype, void* stream);
+
+/*
+ * paged_decode_attention_int8 - paged_decode_attention over an INT8 cache:
+ * the same result with K and V replaced by x_hat = s * x_q.  q and out are
+ * bf16; the codes are widened exactly in registers, the K scale multiplies the
+ * score and the V scale the softmax weight (weights rounded to bf16 as in the
+ * bf16 decode; accumulation in fp32).  Other arguments and the workspace are
+ * as for paged_decode_attention (size it with dtype PKV_INT8, which equals the
+ * bf16 size).
+ */
+int paged_decode_attention_int8(void* out, const void* q,
+                                const int8_t* k_cache, const int8_t* v_cache,
+                                const float* k_scale, const float* v_scale,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int B, int h_q, int h_kv, int d_h, int n_blocks,
+                                int max_blocks_per_seq, int max_context_len, float scale,
+                                int num_splits, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Number of splits paged_decode_attention uses for these arguments; -1 on
  * invalid arguments.  With num_splits == 0 it queries the current device's

@@ -54,6 +54,30 @@ int debug_check_tables(const int32_t* tables, const int32_t* lens, int n_seqs, i
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
+// PKV_DEBUG: slots in range (or negative) and no slot named twice.
+int debug_check_slots(const int64_t* slot_mapping, int T, int n_blocks, hipStream_t stream) {
+  std::vector<int64_t> sl;
+  if (!copy_to_host(sl, slot_mapping, (size_t)T, stream)) return PKV_ERR_HIP;
+  std::vector<char> seen((size_t)n_blocks * 16, 0);
+  for (int64_t v : sl) {
+    if (v < 0) continue;
+    if (v >= (int64_t)n_blocks * 16 || seen[(size_t)v]) return PKV_ERR_INVALID_ARG;
+    seen[(size_t)v] = 1;
+  }
+  return PKV_OK;
+}
+
+// Pool element type of a decode dtype code; false for an unknown code.
+bool kv_type_of(int dtype, pkv::KvType* kv) {
+  if (dtype == PKV_F32) *kv = pkv::KvType::kF32;
+  else if (dtype == PKV_BF16) *kv = pkv::KvType::kBF16;
+  else if (dtype == PKV_INT8) *kv = pkv::KvType::kI8;
+  else return false;
+  return true;
+}
+// The head chunking and workspace of an INT8 cache are those of bf16 rows.
+bool chunks_as_bf16(pkv::KvType kv) { return kv != pkv::KvType::kF32; }
+
 }  // namespace
 
 extern "C" {
@@ -82,17 +106,34 @@ int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
     return PKV_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   if (debug_checks()) {
-    std::vector<int64_t> sl;
-    if (!copy_to_host(sl, slot_mapping, (size_t)T, s)) return PKV_ERR_HIP;
-    std::vector<char> seen((size_t)n_blocks * 16, 0);
-    for (int64_t v : sl) {
-      if (v < 0) continue;
-      if (v >= (int64_t)n_blocks * 16 || seen[(size_t)v]) return PKV_ERR_INVALID_ARG;
-      seen[(size_t)v] = 1;
-    }
+    const int rc = debug_check_slots(slot_mapping, T, n_blocks, s);
+    if (rc != PKV_OK) return rc;
   }
   return from_hip(pkv::launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, T, h_kv, d_h,
                                         n_blocks, eb, s));
+}
+
+int kv_append_int8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                   int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale, int T,
+                   int h_kv, int d_h, int n_blocks, int dtype, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return PKV_ERR_INVALID_ARG;
+  if (T < 0 || h_kv <= 0 || n_blocks <= 0) return PKV_ERR_INVALID_ARG;
+  if (d_h != 64 && d_h != 128) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)T * h_kv * (d_h / 8) > 0x7fffffff - 256) return PKV_ERR_UNSUPPORTED;
+  if (T == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u) || ((uintptr_t)slot_mapping & 7u))
+    return PKV_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (debug_checks()) {
+    const int rc = debug_check_slots(slot_mapping, T, n_blocks, s);
+    if (rc != PKV_OK) return rc;
+  }
+  return from_hip(pkv::launch_kv_append_i8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale,
+                                           v_scale, T, h_kv, d_h, n_blocks, eb, s));
 }
 
 static bool decode_shape_ok(int B, int h_q, int h_kv, int max_context_len, int num_splits) {
@@ -101,9 +142,10 @@ static bool decode_shape_ok(int B, int h_q, int h_kv, int max_context_len, int n
 }
 
 // Automatic split count: one range per wavefront the device holds at once.
-static int auto_splits(int B, int h_q, int h_kv, int d_h, int max_context_len, bool bf16) {
+static int auto_splits(int B, int h_q, int h_kv, int d_h, int max_context_len, pkv::KvType kv) {
+  const bool bf16 = chunks_as_bf16(kv);
   const int gc = pkv::head_chunks(h_q / h_kv, d_h, bf16).per_chunk;
-  int waves = pkv::decode_resident_waves(d_h, bf16, gc);
+  int waves = pkv::decode_resident_waves(d_h, kv, gc);
   if (waves <= 0) waves = 2048;
   const int64_t bound = pkv::decode_split_bound(B, h_q, h_kv, d_h, bf16, max_context_len, 0);
   return (int)(waves < bound ? waves : bound);
@@ -111,41 +153,48 @@ static int auto_splits(int B, int h_q, int h_kv, int d_h, int max_context_len, b
 
 int pkv_decode_num_splits(int B, int h_q, int h_kv, int d_h, int max_context_len, int dtype,
                           int num_splits) {
-  if (!decode_shape_ok(B, h_q, h_kv, max_context_len, num_splits) || elem_bytes(dtype) == 0 ||
+  pkv::KvType kv;
+  if (!decode_shape_ok(B, h_q, h_kv, max_context_len, num_splits) || !kv_type_of(dtype, &kv) ||
       (d_h != 64 && d_h != 128))
     return -1;
   if (num_splits > 0) return num_splits;
-  return auto_splits(B, h_q, h_kv, d_h, max_context_len, dtype == PKV_BF16);
+  return auto_splits(B, h_q, h_kv, d_h, max_context_len, kv);
 }
 
 size_t pkv_decode_workspace_bytes(int B, int h_q, int h_kv, int d_h, int max_context_len,
                                   int dtype, int num_splits) {
+  pkv::KvType kv;
   if (!decode_shape_ok(B, h_q, h_kv, max_context_len, num_splits) || d_h <= 0 ||
-      elem_bytes(dtype) == 0)
+      !kv_type_of(dtype, &kv))
     return 0;
-  return pkv::decode_workspace_bytes(B, h_q, h_kv, d_h, dtype == PKV_BF16, max_context_len,
+  return pkv::decode_workspace_bytes(B, h_q, h_kv, d_h, chunks_as_bf16(kv), max_context_len,
                                      num_splits);
 }
 
-int paged_decode_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
-                           const int32_t* block_tables, const int32_t* context_lens, int B,
-                           int h_q, int h_kv, int d_h, int n_blocks, int max_blocks_per_seq,
-                           int max_context_len, float scale, int dtype, int num_splits,
-                           void* workspace, size_t workspace_bytes, void* stream) {
-  if (elem_bytes(dtype) == 0) return PKV_ERR_INVALID_ARG;
+// Both decode entry points: validation, workspace layout and launch.  k_scale
+// and v_scale are used (and required) for the INT8 cache only.
+static int decode_call(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                       const int32_t* context_lens, int B, int h_q, int h_kv, int d_h,
+                       int n_blocks, int max_blocks_per_seq, int max_context_len, float scale,
+                       pkv::KvType kv, int num_splits, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   if (!decode_shape_ok(B, h_q, h_kv, max_context_len, num_splits) || n_blocks <= 0 ||
       max_blocks_per_seq <= 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * 16 ||
       !isfinite(scale))
     return PKV_ERR_INVALID_ARG;
   if (d_h != 64 && d_h != 128) return PKV_ERR_UNSUPPORTED;
   if (B == 0) return PKV_OK;
-  const bool bf16 = dtype == PKV_BF16;
+  const bool i8 = kv == pkv::KvType::kI8;
+  const bool bf16 = chunks_as_bf16(kv);
   const pkv::HeadChunks hc = pkv::head_chunks(h_q / h_kv, d_h, bf16);
   if ((int64_t)B * h_kv * hc.n_chunks > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens ||
+      (i8 && (!k_scale || !v_scale)))
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u))
+      ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u) ||
+      (i8 && (((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u))))
     return PKV_ERR_INVALID_ARG;
   const size_t need =
       pkv::decode_workspace_bytes(B, h_q, h_kv, d_h, bf16, max_context_len, num_splits);
@@ -161,6 +210,8 @@ int paged_decode_attention(void* out, const void* q, const void* k_cache, const 
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
+  a.k_scale = i8 ? k_scale : nullptr;
+  a.v_scale = i8 ? v_scale : nullptr;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.ws = (float*)workspace;
@@ -175,9 +226,32 @@ int paged_decode_attention(void* out, const void* q, const void* k_cache, const 
   a.gc = hc.per_chunk;
   a.n_blocks = n_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_splits = num_splits > 0 ? num_splits : auto_splits(B, h_q, h_kv, d_h, max_context_len, bf16);
+  a.num_splits = num_splits > 0 ? num_splits : auto_splits(B, h_q, h_kv, d_h, max_context_len, kv);
   a.scale_log2 = scale * kLog2e;
-  return from_hip(pkv::launch_decode(a, d_h, bf16, s));
+  return from_hip(pkv::launch_decode(a, d_h, kv, s));
+}
+
+int paged_decode_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, int B,
+                           int h_q, int h_kv, int d_h, int n_blocks, int max_blocks_per_seq,
+                           int max_context_len, float scale, int dtype, int num_splits,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
+  return decode_call(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, B,
+                     h_q, h_kv, d_h, n_blocks, max_blocks_per_seq, max_context_len, scale,
+                     dtype == PKV_BF16 ? pkv::KvType::kBF16 : pkv::KvType::kF32, num_splits,
+                     workspace, workspace_bytes, stream);
+}
+
+int paged_decode_attention_int8(void* out, const void* q, const int8_t* k_cache,
+                                const int8_t* v_cache, const float* k_scale, const float* v_scale,
+                                const int32_t* block_tables, const int32_t* context_lens, int B,
+                                int h_q, int h_kv, int d_h, int n_blocks, int max_blocks_per_seq,
+                                int max_context_len, float scale, int num_splits, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return decode_call(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, B,
+                     h_q, h_kv, d_h, n_blocks, max_blocks_per_seq, max_context_len, scale,
+                     pkv::KvType::kI8, num_splits, workspace, workspace_bytes, stream);
 }
 
 int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_q,

@@ -70,10 +70,31 @@ struct DecodeShape {
   static_assert(kVPL >= 1 && kPasses % 2 == 0, "lane mapping");
 };
 
+// INT8 cache (codes with one float32 scale per token head row) read by bf16
+// queries: the lane mapping, query words and accumulators are those of bf16
+// rows of the same width, so a lane holds 8 channels (8 bytes) of a token row.
+struct i8_t {};
+template <int D>
+struct DecodeShape<i8_t, D> : DecodeShape<bf16_t, D> {};
+
+// Element type of q and out: the cache's own, bf16 for an INT8 cache.
+template <typename T>
+using OutOf = typename std::conditional<std::is_same<T, i8_t>::value, bf16_t, T>::type;
+
 template <int NP, int VPL>
 struct BlockRegs {
   uint4 k[NP][VPL];
   uint4 v[NP][VPL];
+};
+
+// An INT8 block as one lane holds it: 8 codes of K and of V per pass, and the
+// scales of the pass's token.
+template <int NP>
+struct BlockRegsI8 {
+  uint2 k[NP];
+  uint2 v[NP];
+  float ks[NP];
+  float vs[NP];
 };
 
 __device__ __forceinline__ uint32_t dw(const uint4& u, int w) {
@@ -88,7 +109,16 @@ __device__ __forceinline__ int lane_channel(int sub, int e) {
 }
 
 template <typename T, int D>
-using BlockOf = BlockRegs<DecodeShape<T, D>::kPasses, DecodeShape<T, D>::kVPL>;
+struct BlockSel {
+  using type = BlockRegs<DecodeShape<T, D>::kPasses, DecodeShape<T, D>::kVPL>;
+};
+template <int D>
+struct BlockSel<i8_t, D> {
+  static_assert(DecodeShape<i8_t, D>::kVPL == 1, "one 8-byte chunk per lane and token");
+  using type = BlockRegsI8<DecodeShape<i8_t, D>::kPasses>;
+};
+template <typename T, int D>
+using BlockOf = typename BlockSel<T, D>::type;
 
 // K/V are read exactly once per call, so they are loaded with the non-temporal
 // hint: on MI355X this streams them past the caches' normal allocation and
@@ -98,21 +128,63 @@ __device__ __forceinline__ uint4 stream_load(const uint4* p) {
   return make_uint4(x.x, x.y, x.z, x.w);
 }
 
-// Loads one 16-token block of one KV head; base points at its first vector.
+__device__ __forceinline__ uint2 stream_load(const uint2* p) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(x.x, x.y);
+}
+
+// Loads one 16-token block of one KV head; bh = physical block * h_kv + KV head.
 template <typename T, int D>
-__device__ __forceinline__ void load_block(BlockOf<T, D>& r, const uint4* __restrict__ kbase,
-                                           const uint4* __restrict__ vbase, int slot, int sub) {
+__device__ __forceinline__ void load_block(BlockOf<T, D>& r, const DecodeArgs& a, size_t bh,
+                                           int slot, int sub) {
   using Sh = DecodeShape<T, D>;
+  if constexpr (std::is_same<T, i8_t>::value) {
+    constexpr int kRow = D / 8;  // 8-byte chunks per row of codes
+    const uint2* kbase = reinterpret_cast<const uint2*>(a.k_cache) + bh * (kBlock * kRow);
+    const uint2* vbase = reinterpret_cast<const uint2*>(a.v_cache) + bh * (kBlock * kRow);
 #pragma unroll
-  for (int ps = 0; ps < Sh::kPasses; ++ps)
+    for (int ps = 0; ps < Sh::kPasses; ++ps)
+      r.k[ps] = stream_load(&kbase[(ps * Sh::kTPW + slot) * kRow + sub]);
 #pragma unroll
-    for (int v = 0; v < Sh::kVPL; ++v)
-      r.k[ps][v] = stream_load(&kbase[(ps * Sh::kTPW + slot) * Sh::kRowVec + v * Sh::kLPT + sub]);
+    for (int ps = 0; ps < Sh::kPasses; ++ps)
+      r.v[ps] = stream_load(&vbase[(ps * Sh::kTPW + slot) * kRow + sub]);
 #pragma unroll
-  for (int ps = 0; ps < Sh::kPasses; ++ps)
+    for (int ps = 0; ps < Sh::kPasses; ++ps) {
+      r.ks[ps] = a.k_scale[bh * kBlock + ps * Sh::kTPW + slot];
+      r.vs[ps] = a.v_scale[bh * kBlock + ps * Sh::kTPW + slot];
+    }
+  } else {
+    const size_t head_vecs = (size_t)kBlock * Sh::kRowVec;
+    const uint4* __restrict__ kbase = reinterpret_cast<const uint4*>(a.k_cache) + bh * head_vecs;
+    const uint4* __restrict__ vbase = reinterpret_cast<const uint4*>(a.v_cache) + bh * head_vecs;
 #pragma unroll
-    for (int v = 0; v < Sh::kVPL; ++v)
-      r.v[ps][v] = stream_load(&vbase[(ps * Sh::kTPW + slot) * Sh::kRowVec + v * Sh::kLPT + sub]);
+    for (int ps = 0; ps < Sh::kPasses; ++ps)
+#pragma unroll
+      for (int v = 0; v < Sh::kVPL; ++v)
+        r.k[ps][v] =
+            stream_load(&kbase[(ps * Sh::kTPW + slot) * Sh::kRowVec + v * Sh::kLPT + sub]);
+#pragma unroll
+    for (int ps = 0; ps < Sh::kPasses; ++ps)
+#pragma unroll
+      for (int v = 0; v < Sh::kVPL; ++v)
+        r.v[ps][v] =
+            stream_load(&vbase[(ps * Sh::kTPW + slot) * Sh::kRowVec + v * Sh::kLPT + sub]);
+  }
+}
+
+// Codes c0 (low half) and c1 (high half) as a bf16 pair, exactly: an int8 code
+// converts to float32 without rounding and, being at most 7 significant bits,
+// its float32 pattern ends in 16 zero bits, so the high halves are the bf16
+// values.
+__device__ __forceinline__ uint32_t i8_pair_bf16(int c0, int c1) {
+  return __builtin_amdgcn_perm(__float_as_uint((float)c1), __float_as_uint((float)c0),
+                               0x07060302u);
+}
+// Code k (0..7) of an 8-byte chunk, sign-extended.
+__device__ __forceinline__ int i8_code(const uint2& u, int k) {
+  const uint32_t w = k < 4 ? u.x : u.y;
+  return (int)(int8_t)(w >> (8 * (k & 3)));
 }
 
 // Query registers: bf16 kept packed for v_dot2, fp32 kept as floats (4 words per vector).
@@ -151,7 +223,11 @@ __device__ __forceinline__ void attend_block(const BlockOf<T, D>& r,
     for (int w = 0; w < 4; ++w)
 #pragma unroll
       for (int ps = 0; ps < NP; ++ps) {
-        const uint32_t kw = dw(r.k[ps][v], w);
+        uint32_t kw;
+        if constexpr (std::is_same<T, i8_t>::value)
+          kw = i8_pair_bf16(i8_code(r.k[ps], 2 * w), i8_code(r.k[ps], 2 * w + 1));
+        else
+          kw = dw(r.k[ps][v], w);
 #pragma unroll
         for (int j = 0; j < GC; ++j) {
           if constexpr (std::is_same<T, float>::value)
@@ -184,8 +260,10 @@ __device__ __forceinline__ void attend_block(const BlockOf<T, D>& r,
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps) {
     ok[ps] = !MASK || (ps * Sh::kTPW + slot < valid);
+    float f = scale_log2;
+    if constexpr (std::is_same<T, i8_t>::value) f = r.ks[ps] * scale_log2;  // the token's K scale
 #pragma unroll
-    for (int j = 0; j < GC; ++j) s[ps][j] = (MASK && !ok[ps]) ? kNegInf : s[ps][j] * scale_log2;
+    for (int j = 0; j < GC; ++j) s[ps][j] = (MASK && !ok[ps]) ? kNegInf : s[ps][j] * f;
   }
   bool need = false;
   float smax[GC];
@@ -236,6 +314,34 @@ __device__ __forceinline__ void attend_block(const BlockOf<T, D>& r,
 #pragma unroll
           for (int j = 0; j < GC; ++j) acc[j][v * 4 + w] = fmaf(p[ps][j], x, acc[j][v * 4 + w]);
         }
+    }
+  } else if constexpr (std::is_same<T, i8_t>::value) {
+    // As for bf16 rows, tokens are paired (passes 2i, 2i+1); each weight carries
+    // its token's V scale (p * s_v, rounded to bf16 once), and the codes of the
+    // two tokens at one channel form an exact bf16 pair.  A masked token's
+    // weight is zero whatever its scale slot holds.
+#pragma unroll
+    for (int pr = 0; pr < NP / 2; ++pr) {
+      uint32_t pp[GC];
+#pragma unroll
+      for (int j = 0; j < GC; ++j) {
+        float p0 = p[2 * pr][j] * r.vs[2 * pr];
+        float p1 = p[2 * pr + 1][j] * r.vs[2 * pr + 1];
+        if (MASK) {
+          p0 = ok[2 * pr] ? p0 : 0.f;
+          p1 = ok[2 * pr + 1] ? p1 : 0.f;
+        }
+        pp[j] = pack_bf16x2(p0, p1);
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t x = i8_pair_bf16(i8_code(r.v[2 * pr], c), i8_code(r.v[2 * pr + 1], c));
+#pragma unroll
+        for (int j = 0; j < GC; ++j)
+          acc[j][c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp[j]),
+                                                      __builtin_bit_cast(bf16x2_t, x), acc[j][c],
+                                                      false);
+      }
     }
   } else {
     // Tokens are paired (passes 2i, 2i+1): word (V_t0[c], V_t1[c]) against
@@ -405,11 +511,12 @@ __device__ __forceinline__ void merge_segment_head(const DecodeArgs& a, const Li
     }
     inv = 1.f / ls;
   }
-  T* out = reinterpret_cast<T*>(a.out) + ((size_t)b * a.h_q + head0 + j) * D;
+  using O = OutOf<T>;
+  O* out = reinterpret_cast<O*>(a.out) + ((size_t)b * a.h_q + head0 + j) * D;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int c = lane + i * kWave;
-    if (c < D) store_elem<T>(out, c, o[i] * inv);
+    if (c < D) store_elem<O>(out, c, o[i] * inv);
   }
 }
 
@@ -525,9 +632,10 @@ struct RangeStream {
       if (j >= c.nh || slot_id != 0) continue;
       if (whole) {
         const float inv = 1.f / ls;
-        T* out = reinterpret_cast<T*>(a.out) + ((size_t)p.b * a.h_q + c.head0 + j) * D;
+        using O = OutOf<T>;
+        O* out = reinterpret_cast<O*>(a.out) + ((size_t)p.b * a.h_q + c.head0 + j) * D;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) store_elem<T>(out, lane_channel<T, D>(sub, e), acc[j][e] * inv);
+        for (int e = 0; e < EPL; ++e) store_elem<O>(out, lane_channel<T, D>(sub, e), acc[j][e] * inv);
       } else {
         float* ws = a.ws + ((size_t)(W * 2 + slot) * GC + j) * (D + 2);
 #pragma unroll
@@ -545,11 +653,8 @@ struct RangeStream {
     const int HC = a.h_kv * a.n_chunks;
     const int sub = lane % Sh::kLPT;
     const int slot_id = lane / Sh::kLPT;
-    const uint4* kc4 = reinterpret_cast<const uint4*>(a.k_cache);
-    const uint4* vc4 = reinterpret_cast<const uint4*>(a.v_cache);
-    const size_t head_vecs = (size_t)kBlock * Sh::kRowVec;
-    auto block_base = [&](int raw_entry, int kvh) {
-      return ((size_t)clamp_block(a, raw_entry) * a.h_kv + kvh) * head_vecs;
+    auto block_head = [&](int raw_entry, int kvh) {
+      return (size_t)clamp_block(a, raw_entry) * a.h_kv + kvh;
     };
 
     Ctx cc = ctx_of(a, cur);
@@ -585,16 +690,14 @@ struct RangeStream {
 
     BlockOf<T, D> A, B;
     {
-      const size_t base = block_base(table_entry(cc, t), cc.kvh);
-      load_block<T, D>(A, kc4 + base, vc4 + base, slot_id, sub);
+      load_block<T, D>(A, a, block_head(table_entry(cc, t), cc.kvh), slot_id, sub);
     }
 
     // Block t (in X) is not the piece's last: load block t + 1 (entry in E)
     // into Y, request the entry of block t + 3 into E, then attend block t.
     // A block before the last is always full.
     auto step_in = [&](BlockOf<T, D>& X, BlockOf<T, D>& Y, int& E) {
-      const size_t base = block_base(E, cc.kvh);
-      load_block<T, D>(Y, kc4 + base, vc4 + base, slot_id, sub);
+      load_block<T, D>(Y, a, block_head(E, cc.kvh), slot_id, sub);
       E = table_entry(cc, min(t + 3, cur.j1 - 1));
       attend_block<T, D, GC, false>(X, q, m, l, acc, a.scale_log2, slot_id, kBlock);
       ++t;
@@ -604,8 +707,7 @@ struct RangeStream {
     // past the context.
     auto step_last = [&](BlockOf<T, D>& X, BlockOf<T, D>& Y) {
       if (nxt.valid) {
-        const size_t base = block_base(nxt_blk0, nc.kvh);
-        load_block<T, D>(Y, kc4 + base, vc4 + base, slot_id, sub);
+        load_block<T, D>(Y, a, block_head(nxt_blk0, nc.kvh), slot_id, sub);
       }
       const int valid = cc.L - t * kBlock;
       if (valid >= kBlock)
@@ -679,8 +781,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // Sequences of length 0 get an all-zero output (sequence b by wave b mod splits).
   for (int b0 = W; b0 < a.B; b0 += a.num_splits) {
     if (seq_len(a, b0) != 0) continue;
-    T* out = reinterpret_cast<T*>(a.out) + (size_t)b0 * a.h_q * D;
-    for (int i = lane; i < a.h_q * D; i += kWave) store_elem<T>(out, i, 0.f);
+    OutOf<T>* out = reinterpret_cast<OutOf<T>*>(a.out) + (size_t)b0 * a.h_q * D;
+    for (int i = lane; i < a.h_q * D; i += kWave) store_elem<OutOf<T>>(out, i, 0.f);
   }
 
   const ScanResult all = scan_blocks(a, -1, lane);
@@ -806,9 +908,14 @@ static hipError_t dispatch_gc(const DecodeArgs& a, hipStream_t stream, int* wave
   return hipErrorInvalidValue;
 }
 
-static hipError_t dispatch(const DecodeArgs& a, int d_h, bool bf16, hipStream_t stream,
+static hipError_t dispatch(const DecodeArgs& a, int d_h, KvType kv, hipStream_t stream,
                            int* waves_out) {
-  if (bf16) {
+  if (kv == KvType::kI8) {
+    if (d_h == 64) return dispatch_gc<i8_t, 64>(a, stream, waves_out);
+    if (d_h == 128) return dispatch_gc<i8_t, 128>(a, stream, waves_out);
+    return hipErrorInvalidValue;
+  }
+  if (kv == KvType::kBF16) {
     if (d_h == 64) return dispatch_gc<bf16_t, 64>(a, stream, waves_out);
     if (d_h == 128) return dispatch_gc<bf16_t, 128>(a, stream, waves_out);
   } else {
@@ -818,16 +925,16 @@ static hipError_t dispatch(const DecodeArgs& a, int d_h, bool bf16, hipStream_t 
   return hipErrorInvalidValue;
 }
 
-int decode_resident_waves(int d_h, bool bf16, int gc) {
+int decode_resident_waves(int d_h, KvType kv, int gc) {
   DecodeArgs a{};
   a.gc = gc;
   int waves = 0;
-  if (dispatch(a, d_h, bf16, nullptr, &waves) != hipSuccess) return 0;
+  if (dispatch(a, d_h, kv, nullptr, &waves) != hipSuccess) return 0;
   return waves;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int d_h, bool bf16, hipStream_t stream) {
-  return dispatch(a, d_h, bf16, stream, nullptr);
+hipError_t launch_decode(const DecodeArgs& a, int d_h, KvType kv, hipStream_t stream) {
+  return dispatch(a, d_h, kv, stream, nullptr);
 }
 
 }  // namespace pkv

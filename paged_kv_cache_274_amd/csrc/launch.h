@@ -63,11 +63,17 @@ inline size_t decode_workspace_bytes(int B, int h_q, int h_kv, int d_h, bool bf1
          ((segs * 2 * sizeof(int32_t) + 15) / 16) * 16 + 16;
 }
 
+// Element type of a KV pool.  kI8: int8 codes with a float32 scale per token
+// head row, read by bf16 queries.
+enum class KvType { kF32, kBF16, kI8 };
+
 struct DecodeArgs {
   void* out;
   const void* q;
   const void* k_cache;
   const void* v_cache;
+  const float* k_scale;  // kI8 only: [n_blocks, h_kv, 16]
+  const float* v_scale;
   const int32_t* block_tables;
   const int32_t* context_lens;
   float* ws;  // [num_splits][2][gc][d_h + 2]: accumulators, max (log2 units), sum
@@ -79,14 +85,22 @@ struct DecodeArgs {
 
 // Wavefronts of the decode kernel for (d_h, dtype, gc) that the current device
 // holds at once; 0 if it cannot be queried.
-int decode_resident_waves(int d_h, bool bf16, int gc);
+int decode_resident_waves(int d_h, KvType kv, int gc);
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                             void* k_cache, void* v_cache, int T, int h_kv, int d_h,
                             int n_blocks, int elem_bytes, hipStream_t stream);
 
 // Returns hipErrorInvalidValue for (dtype, d_h, gc) combinations without a kernel.
-hipError_t launch_decode(const DecodeArgs& a, int d_h, bool bf16, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int d_h, KvType kv, hipStream_t stream);
+
+// Quantises each new token's K and V rows to int8 with a float32 scale per
+// (token, KV head) row and scatters codes and scales to their slots.  src_bytes:
+// 2 (bf16 rows) or 4 (float32 rows).
+hipError_t launch_kv_append_i8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                               int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale,
+                               int T, int h_kv, int d_h, int n_blocks, int src_bytes,
+                               hipStream_t stream);
 
 struct PrefillArgs {
   void* out;

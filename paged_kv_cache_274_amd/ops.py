@@ -17,9 +17,11 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
-PKV_F32, PKV_BF16 = 0, 1
+PKV_F32, PKV_BF16, PKV_INT8 = 0, 1, 2
 _DTYPE = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
+_WS_DTYPE = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.int8: PKV_INT8}
 EXPORTED = ("kv_append", "paged_decode_attention", "paged_prefill_attention",
+            "kv_append_int8", "paged_decode_attention_int8",
             "pkv_decode_workspace_bytes", "pkv_decode_num_splits", "pkv_status_string")
 
 _lib = None
@@ -55,6 +57,12 @@ def lib() -> ctypes.CDLL:
     L.paged_prefill_attention.argtypes = [vp, vp, i32p, vp, vp, i32p, i32p, i32, i32, i32, i32, i32,
                                           i32, i32, i32, ctypes.c_float, i32, vp]
     L.paged_prefill_attention.restype = i32
+    L.kv_append_int8.argtypes = [vp, vp, i64p, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    L.kv_append_int8.restype = i32
+    L.paged_decode_attention_int8.argtypes = [vp, vp, vp, vp, vp, vp, i32p, i32p, i32, i32, i32,
+                                              i32, i32, i32, i32, ctypes.c_float, i32, vp,
+                                              ctypes.c_size_t, vp]
+    L.paged_decode_attention_int8.restype = i32
     _lib = L
     return L
 
@@ -106,14 +114,85 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tens
 
 def decode_num_splits(B: int, h_q: int, h_kv: int, d_h: int, max_context_len: int,
                       dtype: torch.dtype = torch.bfloat16, num_splits: int = 0) -> int:
-    return int(lib().pkv_decode_num_splits(B, h_q, h_kv, d_h, max_context_len, _DTYPE[dtype],
+    """dtype: the pool's (torch.int8 for the INT8 cache)."""
+    return int(lib().pkv_decode_num_splits(B, h_q, h_kv, d_h, max_context_len, _WS_DTYPE[dtype],
                                            num_splits))
 
 
 def decode_workspace_bytes(B: int, h_q: int, h_kv: int, d_h: int, max_context_len: int,
                            dtype: torch.dtype = torch.bfloat16, num_splits: int = 0) -> int:
-    return int(lib().pkv_decode_workspace_bytes(B, h_q, h_kv, d_h, max_context_len, _DTYPE[dtype],
-                                                 num_splits))
+    """dtype: the pool's (torch.int8 for the INT8 cache)."""
+    return int(lib().pkv_decode_workspace_bytes(B, h_q, h_kv, d_h, max_context_len,
+                                                 _WS_DTYPE[dtype], num_splits))
+
+
+def _scale_pools(k_scale: torch.Tensor, v_scale: torch.Tensor, n_blocks: int, h_kv: int):
+    _need(k_scale.dtype == torch.float32 and v_scale.dtype == torch.float32 and
+          k_scale.shape == (n_blocks, h_kv, 16) and v_scale.shape == k_scale.shape and
+          k_scale.is_contiguous() and v_scale.is_contiguous(),
+          "k_scale/v_scale must be contiguous float32 [n_blocks, h_kv, 16]")
+
+
+def kv_append_int8(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                   v_scale: torch.Tensor) -> None:
+    """Quantise new K/V rows [T, h_kv, d_h] (bf16 or fp32) into the INT8 pools
+    (int8 [n_blocks, h_kv, 16, d_h]) and their scales, in place."""
+    n_blocks, h_kv, d = _pool_shape(k_cache, v_cache)
+    _need(k_cache.dtype == torch.int8, "the INT8 pools must be int8")
+    _scale_pools(k_scale, v_scale, n_blocks, h_kv)
+    _dev(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale)
+    _need(k_new.dim() == 3 and k_new.shape[1:] == (h_kv, d) and v_new.shape == k_new.shape,
+          "k_new/v_new must be [T, h_kv, d_h]")
+    _need(k_new.dtype == v_new.dtype and k_new.dtype in _DTYPE, "k_new/v_new: bf16 or fp32")
+    _need(k_new.is_contiguous() and v_new.is_contiguous(), "k_new/v_new must be contiguous")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (k_new.shape[0],),
+          "slot_mapping must be int64 [T]")
+    rc = lib().kv_append_int8(k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(),
+                              k_cache.data_ptr(), v_cache.data_ptr(), k_scale.data_ptr(),
+                              v_scale.data_ptr(), int(k_new.shape[0]), h_kv, d, n_blocks,
+                              _DTYPE[k_new.dtype], _stream(k_cache))
+    if rc != 0:
+        raise PkvError("kv_append_int8", rc)
+
+
+def paged_decode_attention_int8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                k_scale: torch.Tensor, v_scale: torch.Tensor,
+                                block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                max_context_len: int, scale: Optional[float] = None,
+                                num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Single-token decode over the INT8 cache.  q, out: bf16 [B, h_q, d_h]."""
+    n_blocks, h_kv, d = _pool_shape(k_cache, v_cache)
+    _need(k_cache.dtype == torch.int8, "the INT8 pools must be int8")
+    _scale_pools(k_scale, v_scale, n_blocks, h_kv)
+    _need(q.dim() == 3 and q.shape[2] == d and q.dtype == torch.bfloat16,
+          "q must be bf16 [B, h_q, d_h]")
+    B, h_q = int(q.shape[0]), int(q.shape[1])
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == B, "block_tables must be int32 [B, max_blocks]")
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (B,),
+          "context_lens must be int32 [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _dev(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_bytes = decode_workspace_bytes(B, h_q, h_kv, d, int(max_context_len), torch.int8,
+                                      num_splits)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().paged_decode_attention_int8(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_scale.data_ptr(),
+        v_scale.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, h_q, h_kv, d,
+        n_blocks, int(block_tables.shape[1]), int(max_context_len), float(scale),
+        int(num_splits), ws_ptr, ws_len, _stream(q))
+    if rc != 0:
+        raise PkvError("paged_decode_attention_int8", rc)
+    return out
 
 
 def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

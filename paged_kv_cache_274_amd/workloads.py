@@ -256,3 +256,34 @@ def config(k: int, *, poison: bool = False) -> Workload:
         return build(name, rng, dtype="bf16", h_q=14, h_kv=2, d=64, decode_lens=lens,
                      prefill=[(512, 512)] * 4, free_frac=0.10, poison=poison)
     raise ValueError(f"no config {k}")
+
+
+@dataclass
+class Int8Pools:
+    """An INT8 cache beside a workload: codes int8 ``[n_blocks, h_kv, 16, d]`` and
+    float32 scales ``[n_blocks, h_kv, 16]`` for K and for V."""
+    k_codes: torch.Tensor
+    v_codes: torch.Tensor
+    k_scales: torch.Tensor
+    v_scales: torch.Tensor
+
+
+def int8_pools(w: Workload, seed: int, poison: bool = False) -> Int8Pools:
+    """Random INT8 pools of the workload's shape: codes uniform on [-127, 127] and
+    scales uniform on [0.005, 0.03] (the scale range that rows of N(0,1) values
+    get), drawn with ``default_rng(seed)`` in the order K codes, V codes, K
+    scales, V scales.  These are draws, not the quantisation of anything.  With
+    ``poison=True`` the scales of every slot the workload's bf16 pool marks
+    unused (NaN there) are NaN, so an unmasked read shows up as NaN."""
+    rng = np.random.default_rng(seed)
+    shape = tuple(w.k_cache.shape)
+    kq = rng.integers(-127, 128, size=shape).astype(np.int8)
+    vq = rng.integers(-127, 128, size=shape).astype(np.int8)
+    ks = rng.uniform(0.005, 0.03, size=shape[:3]).astype(np.float32)
+    vs = rng.uniform(0.005, 0.03, size=shape[:3]).astype(np.float32)
+    if poison:
+        unused = torch.isnan(w.k_cache[..., 0].float()).numpy()
+        ks[unused] = np.nan
+        vs[unused] = np.nan
+    return Int8Pools(torch.from_numpy(kq), torch.from_numpy(vq), torch.from_numpy(ks),
+                     torch.from_numpy(vs))

@@ -125,3 +125,47 @@ def test_workspace_bound(B, h_q, h_kv, d, maxc, dtype):
     assert ws(-1) == 0
     assert ws((1 << 16) + 1) == 0
     assert ops.decode_num_splits(B, h_q, h_kv, d, maxc, dtype, num_splits=48) == 48
+
+
+def _append8(**kw):
+    a = dict(k_new=FAKE, v_new=FAKE, slots=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, T=4, h_kv=2,
+             d=64, nb=8, dt=1)
+    a.update(kw)
+    return ops.lib().kv_append_int8(a["k_new"], a["v_new"], a["slots"], a["kc"], a["vc"], a["ks"],
+                                    a["vs"], a["T"], a["h_kv"], a["d"], a["nb"], a["dt"], None)
+
+
+def test_kv_append_int8_validation():
+    assert _append8(dt=2) == 1          # the source rows are bf16 or fp32
+    assert _append8(ks=None) == 1
+    assert _append8(vs=FAKE + 2) == 1
+    assert _append8(kc=MISALIGNED) == 1
+    assert _append8(d=96) == 2
+    assert _append8(T=-1) == 1
+    assert _append8(T=0, k_new=None, v_new=None) == 0
+
+
+def _decode8(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, tbl=FAKE, lens=FAKE, B=4,
+             h_q=8, h_kv=2, d=128, nb=64, mb=16, maxc=256, scale=0.1, P=0, ws=FAKE,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    return ops.lib().paged_decode_attention_int8(
+        a["out"], a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["tbl"], a["lens"], a["B"],
+        a["h_q"], a["h_kv"], a["d"], a["nb"], a["mb"], a["maxc"], a["scale"], a["P"], a["ws"],
+        a["ws_bytes"], None)
+
+
+def test_decode_int8_validation():
+    assert _decode8(ks=None) == 1
+    assert _decode8(vs=FAKE + 1) == 1
+    assert _decode8(d=80) == 2
+    assert _decode8(h_q=6, h_kv=4) == 1
+    assert _decode8(ws=None, P=16) == 3
+    assert _decode8(B=0, out=None, q=None) == 0
+    # the INT8 cache sizes its workspace like bf16 rows
+    for n in (0, 16):
+        assert (ops.decode_workspace_bytes(4, 8, 2, 128, 256, torch.int8, n) ==
+                ops.decode_workspace_bytes(4, 8, 2, 128, 256, torch.bfloat16, n))
+    assert ops.lib().paged_decode_attention(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 2, 128, 64,
+                                            16, 256, 0.1, 2, 0, FAKE, 1 << 30, None) == 1

@@ -1,0 +1,142 @@
+"""Parity of the INT8 KV cache (HIP path through the C ABI) with the CPU oracle.
+
+kv_append_int8 must match the oracle's codes and scales bit for bit (the codes
+are integers decided in float32 by both sides, with the same division and the
+same rounding).  Decode over the INT8 cache must be within 2e-2 of the float64
+oracle's attention over the dequantised cache, like the bf16 decode: the
+queries are bf16 and each softmax weight times its V scale is rounded to bf16
+once.  Scales of unused slots are NaN, so an unmasked read shows up.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.quant as Q
+import pins
+from gpu_run import bits, max_err
+from paged_kv_cache_274_amd import ops
+from paged_kv_cache_274_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 2e-2
+
+
+def _f32(t: torch.Tensor) -> np.ndarray:
+    return t.float().numpy()
+
+
+def _append(w, pools, slots=None):
+    """GPU and oracle append of the workload's new tokens; returns both pool sets."""
+    slots = w.slot_mapping if slots is None else slots
+    g = [t.to(DEV) for t in (pools.k_codes, pools.v_codes, pools.k_scales, pools.v_scales)]
+    ops.kv_append_int8(w.k_new.to(DEV), w.v_new.to(DEV), slots.to(DEV), *g)
+    torch.cuda.synchronize()
+    got = [t.cpu() for t in g]
+    ref = Q.kv_append_int8(_f32(w.k_new), _f32(w.v_new), slots.numpy(), pools.k_codes.numpy(),
+                           pools.v_codes.numpy(), pools.k_scales.numpy(), pools.v_scales.numpy())
+    return got, ref
+
+
+def _check_append_exact(got, ref):
+    for g, r in zip(got, ref):
+        r = torch.from_numpy(np.ascontiguousarray(r))
+        if g.dtype == torch.int8:
+            assert torch.equal(g, r)
+        else:
+            assert torch.equal(torch.isnan(g), torch.isnan(r))
+            assert torch.equal(g.view(torch.int32), r.view(torch.int32))
+
+
+def _decode(w, pools_dev, splits=0, lens=None):
+    lens = w.dec_context_lens if lens is None else lens
+    out = ops.paged_decode_attention_int8(
+        w.dec_q.to(DEV), *pools_dev, w.dec_block_tables.to(DEV), lens.to(DEV),
+        max(int(lens.max()), 0) if len(lens) else 0, scale=w.scale, num_splits=splits)
+    return out.cpu()
+
+
+def _oracle_decode(w, ref, lens=None):
+    lens = w.dec_context_lens if lens is None else lens
+    return Q.decode_int8(pins.np64(w.dec_q), *ref, w.dec_block_tables.numpy(), lens.numpy(),
+                         w.scale)
+
+
+# ----------------------------------------------------------------------------- append
+
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+@pytest.mark.parametrize("d,h_kv", [(64, 2), (128, 8), (128, 1), (64, 4)])
+def test_append_int8_bit_exact(src, d, h_kv):
+    rng = np.random.default_rng(300 + d + h_kv)
+    lens = [1, 16, 17, 40, 100, 33, 64]
+    w = W.build("app8", rng, dtype=src, h_q=h_kv * 2, h_kv=h_kv, d=d, decode_lens=lens,
+                free_frac=0.3, poison=True)
+    # rows that decide the rounding rule: max 127 then exact ties; an all-zero
+    # row (the 1e-8 floor); a huge and a tiny row
+    k_new = w.k_new.clone()
+    k_new[0, 0, :6] = torch.tensor([127.0, 1.5, 2.5, -0.5, -3.5, 126.5])
+    k_new[0, 0, 6:] = 0.0
+    k_new[1, 0] = 0.0
+    k_new[2, 0] *= 3000.0
+    k_new[3, 0] *= 1e-6
+    w.k_new = k_new
+    slots = w.slot_mapping.clone()
+    slots[4] = -1  # padding: nothing written for that token
+    pools = W.int8_pools(w, seed=7, poison=True)
+    got, ref = _append(w, pools, slots)
+    _check_append_exact(got, ref)
+
+
+# ----------------------------------------------------------------------------- decode
+
+DECODE_GRID8 = [
+    # d, h_q, h_kv
+    (64, 4, 4), (64, 14, 2), (128, 32, 8), (128, 6, 2), (64, 40, 8), (128, 16, 1), (64, 12, 4),
+    (128, 8, 1),
+]
+
+
+@pytest.mark.parametrize("d,h_q,h_kv", DECODE_GRID8)
+@pytest.mark.parametrize("splits", [0, 1, 13, 300])
+def test_decode_int8_grid(d, h_q, h_kv, splits):
+    rng = np.random.default_rng(2000 + d + h_q * 7 + h_kv)
+    lens = [1, 15, 16, 17, 63, 64, 65, 200, 333, 700]
+    w = W.build("grid8", rng, dtype="bf16", h_q=h_q, h_kv=h_kv, d=d, decode_lens=lens,
+                free_frac=0.2, max_blocks_per_seq=50, poison=True)
+    pools = W.int8_pools(w, seed=11, poison=True)
+    got, ref = _append(w, pools)
+    _check_append_exact(got, ref)
+    out = _decode(w, [t.to(DEV) for t in got], splits)
+    err = max_err(out, _oracle_decode(w, ref))
+    assert err <= TOL, f"int8 decode max|err| {err}"
+
+
+@pytest.mark.parametrize("k", [3, 5])
+def test_decode_int8_configs(k):
+    """The decode legs of configs 3 and 5 with an INT8 cache, full size."""
+    w = W.config(k, poison=True)
+    pools = W.int8_pools(w, seed=100 + k, poison=True)
+    got, ref = _append(w, pools)
+    _check_append_exact(got, ref)
+    out = _decode(w, [t.to(DEV) for t in got])
+    err = max_err(out, _oracle_decode(w, ref))
+    print(f"config {k} int8: decode max|err| = {err:.3g}")
+    assert err <= TOL
+
+
+def test_decode_int8_zero_length_and_split_agreement():
+    rng = np.random.default_rng(12)
+    w = W.build("z8", rng, dtype="bf16", h_q=8, h_kv=2, d=128, decode_lens=[1, 40, 1, 2000],
+                free_frac=0.5, poison=True)
+    pools = W.int8_pools(w, seed=13, poison=True)
+    got, ref = _append(w, pools)
+    dev = [t.to(DEV) for t in got]
+    lens0 = torch.tensor([0, 40, 0, 2000], dtype=torch.int32)
+    out = _decode(w, dev, 0, lens0)
+    assert torch.count_nonzero(out[0]) == 0 and torch.count_nonzero(out[2]) == 0
+    assert max_err(out, _oracle_decode(w, ref, lens0)) <= TOL
+    a = _decode(w, dev, 1)
+    for splits in (2, 7, 64, 0):
+        assert max_err(_decode(w, dev, splits), a.double().numpy()) <= TOL
+    # one wave per sequence reduces in a fixed order: repeatable bit for bit
+    assert torch.equal(bits(a), bits(_decode(w, dev, 1)))

@@ -144,7 +144,7 @@ int paged_decode_attention(void* out, const void* q,
  *   k_cache, v_cache : device int8 [n_blocks, h_kv, 16, d_h] (codes, laid out
  *                      like the bf16 pools)
  *   k_scale, v_scale : device float32 [n_blocks, h_kv, 16] (s of each row),
- *                      4-byte aligned
+ *                      16-byte aligned (kv_append_int8 needs 4)
  */
 
 /*

@@ -194,7 +194,7 @@ static int decode_call(void* out, const void* q, const void* k_cache, const void
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
       ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u) ||
-      (i8 && (((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u))))
+      (i8 && (!aligned16(k_scale) || !aligned16(v_scale))))
     return PKV_ERR_INVALID_ARG;
   const size_t need =
       pkv::decode_workspace_bytes(B, h_q, h_kv, d_h, bf16, max_context_len, num_splits);

@@ -88,7 +88,9 @@ struct BlockRegs {
 };
 
 // An INT8 block as one lane holds it: 8 codes of K and of V per pass, and the
-// scales of the pass's token.
+// scales of the pass's token.  In an INT8 block the lanes of slot s hold the
+// NP consecutive tokens s * NP .. s * NP + NP - 1 (pass ps: token s * NP + ps),
+// so their scales are one contiguous load.
 template <int NP>
 struct BlockRegsI8 {
   uint2 k[NP];
@@ -96,6 +98,11 @@ struct BlockRegsI8 {
   float ks[NP];
   float vs[NP];
 };
+template <typename T, int D>
+__device__ __forceinline__ int token_of(int ps, int slot) {
+  using Sh = DecodeShape<T, D>;
+  return std::is_same<T, i8_t>::value ? slot * Sh::kPasses + ps : ps * Sh::kTPW + slot;
+}
 
 __device__ __forceinline__ uint32_t dw(const uint4& u, int w) {
   return w == 0 ? u.x : (w == 1 ? u.y : (w == 2 ? u.z : u.w));
@@ -145,14 +152,23 @@ __device__ __forceinline__ void load_block(BlockOf<T, D>& r, const DecodeArgs& a
     const uint2* vbase = reinterpret_cast<const uint2*>(a.v_cache) + bh * (kBlock * kRow);
 #pragma unroll
     for (int ps = 0; ps < Sh::kPasses; ++ps)
-      r.k[ps] = stream_load(&kbase[(ps * Sh::kTPW + slot) * kRow + sub]);
+      r.k[ps] = stream_load(&kbase[token_of<T, D>(ps, slot) * kRow + sub]);
 #pragma unroll
     for (int ps = 0; ps < Sh::kPasses; ++ps)
-      r.v[ps] = stream_load(&vbase[(ps * Sh::kTPW + slot) * kRow + sub]);
-#pragma unroll
-    for (int ps = 0; ps < Sh::kPasses; ++ps) {
-      r.ks[ps] = a.k_scale[bh * kBlock + ps * Sh::kTPW + slot];
-      r.vs[ps] = a.v_scale[bh * kBlock + ps * Sh::kTPW + slot];
+      r.v[ps] = stream_load(&vbase[token_of<T, D>(ps, slot) * kRow + sub]);
+    static_assert(Sh::kPasses == 2 || Sh::kPasses == 4, "scales as one 8- or 16-byte load");
+    const float* ksp = a.k_scale + bh * kBlock + slot * Sh::kPasses;
+    const float* vsp = a.v_scale + bh * kBlock + slot * Sh::kPasses;
+    if constexpr (Sh::kPasses == 4) {
+      const float4 k4 = *reinterpret_cast<const float4*>(ksp);
+      const float4 v4 = *reinterpret_cast<const float4*>(vsp);
+      r.ks[0] = k4.x; r.ks[1] = k4.y; r.ks[2] = k4.z; r.ks[3] = k4.w;
+      r.vs[0] = v4.x; r.vs[1] = v4.y; r.vs[2] = v4.z; r.vs[3] = v4.w;
+    } else {
+      const float2 k2 = *reinterpret_cast<const float2*>(ksp);
+      const float2 v2 = *reinterpret_cast<const float2*>(vsp);
+      r.ks[0] = k2.x; r.ks[1] = k2.y;
+      r.vs[0] = v2.x; r.vs[1] = v2.y;
     }
   } else {
     const size_t head_vecs = (size_t)kBlock * Sh::kRowVec;
@@ -259,7 +275,7 @@ __device__ __forceinline__ void attend_block(const BlockOf<T, D>& r,
   bool ok[NP];
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps) {
-    ok[ps] = !MASK || (ps * Sh::kTPW + slot < valid);
+    ok[ps] = !MASK || (token_of<T, D>(ps, slot) < valid);
     float f = scale_log2;
     if constexpr (std::is_same<T, i8_t>::value) f = r.ks[ps] * scale_log2;  // the token's K scale
 #pragma unroll

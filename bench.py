@@ -25,6 +25,10 @@ Printed as one JSON line:
              still match the ones it was taken on
   prefill    paged_prefill_attention on the mixed Qwen2.5-0.5B-shaped batch
              (4 prompts x 512 tokens, h_q=14, h_kv=2, d_h=64) in TFLOP/s
+  int8_decode  paged_decode_attention_int8 on the same decode step over an
+             INT8 cache: bytes = sum_b L_b * 2 * h_kv * (d_h + 4) (codes and
+             one float32 scale per token head row), time over back-to-back
+             calls, and kv_append_int8 of the step's new tokens
   cpu_baseline  the CPU oracle on the same decode step, on one host core.
 
 Counter runs and their summaries (written to profiles/):
@@ -87,6 +91,12 @@ def digest(names) -> str:
 def kv_bytes(w: W.Workload) -> int:
     """Algorithmic KV bytes one decode call reads: 2 * h_kv * d_h * elem per context token."""
     return int(w.dec_context_lens.to(torch.int64).sum()) * 2 * w.h_kv * w.d * w.elem_bytes
+
+
+def kv_bytes_int8(w: W.Workload) -> int:
+    """Algorithmic bytes one INT8-cache decode call reads: per context token and
+    KV head, d_h codes and one float32 scale, for K and for V."""
+    return int(w.dec_context_lens.to(torch.int64).sum()) * 2 * w.h_kv * (w.d + 4)
 
 
 def prefill_flops(w: W.Workload) -> int:
@@ -185,6 +195,44 @@ def time_decode_calls(r: Resident, iters: int, warmup: int = 3):
     a.record()
     for i in range(iters):
         r.decode(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+class ResidentInt8:
+    """An INT8 cache of the workload's shape (random codes and scales), `copies`
+    rotated device copies, for the INT8 decode leg."""
+
+    def __init__(self, r: Resident, copies: int, seed: int = 8):
+        w = r.w
+        self.r = r
+        dev = r.q.device
+        self.pools = []
+        for c in range(copies):
+            p = W.int8_pools(w, seed=seed + c)
+            self.pools.append([t.to(dev) for t in (p.k_codes, p.v_codes, p.k_scales, p.v_scales)])
+
+    def decode(self, i: int):
+        r = self.r
+        ops.paged_decode_attention_int8(r.q, *self.pools[i % len(self.pools)], r.tables, r.lens,
+                                        r.w.dec_max_context_len, scale=r.w.scale, out=r.out,
+                                        workspace=r.ws)
+
+    def append(self, i: int):
+        r = self.r
+        ops.kv_append_int8(r.k_new, r.v_new, r.slots, *self.pools[i % len(self.pools)])
+
+
+def time_calls(fn, iters: int, warmup: int = 3) -> float:
+    """Average ms of one call over `iters` back-to-back calls (two HIP events)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(iters):
+        fn(i)
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / iters
@@ -400,9 +448,13 @@ def summarize_stats(stats_csv, bench_json, extra):
         for r in csv.DictReader(f):
             if "pkv::" in r["Name"]:
                 rows.append(r)
-    split = [r for r in rows if "decode_split_kernel" in r["Name"]]
-    comb = [r for r in rows if "decode_combine_kernel" in r["Name"]]
+    # the bf16 decode call (the roofline's); the INT8 leg's kernels are listed apart
+    is_bf16 = lambda r: "bf16_t" in r["Name"]  # noqa: E731
+    split = [r for r in rows if "decode_split_kernel" in r["Name"] and is_bf16(r)]
+    comb = [r for r in rows if "decode_combine_kernel" in r["Name"] and is_bf16(r)]
     call_ns = sum(float(r["AverageNs"]) for r in split + comb)
+    i8 = [r for r in rows if "decode_" in r["Name"] and "i8_t" in r["Name"]]
+    i8_ns = sum(float(r["AverageNs"]) for r in i8)
     text = [
         f"# Kernel time of the benchmark run ({line['config']['workload']})",
         "# command (repository root, on the GPU):",
@@ -419,6 +471,8 @@ def summarize_stats(stats_csv, bench_json, extra):
         f"# decode call = split pass + combine pass averages: {call_ns / 1e3:.2f} us (rocprofv3);",
         f"# HIP events in the same run: {line['roofline']['avg_us']} us per call over back-to-back "
         f"calls, {line['roofline']['in_step_avg_us']} us around single calls inside the steps",
+        f"# INT8-cache decode call (split + combine averages over all its calls, warm-up included): {i8_ns / 1e3:.2f} us;"
+        f" HIP events: {line.get('int8_decode', {}).get('avg_us')} us",
         f"decode_call_rocprof_us: {call_ns / 1e3:.3f}",
         f"decode_call_events_us: {line['roofline']['avg_us']}",
         f"bench_value_GBps: {line['value']}",
@@ -505,7 +559,15 @@ def main(argv=None):
     app_ms, dec_ms = time_step_parts(rk, args.steps)
     achieved = kvb / dec_avg_s / 1e9
     app_bytes = 2 * wk.T * wk.h_kv * wk.d * wk.elem_bytes * 2 + wk.T * 8
-    del rk
+    del rk.pools
+    torch.cuda.empty_cache()
+    r8 = ResidentInt8(rk, args.copies)
+    # the INT8 leg reaches its steady rate only after a few hundred calls (the
+    # first 30 average over twice the steady time), so it warms up longer
+    i8_ms = time_calls(r8.decode, args.steps, warmup=300)
+    i8_app_ms = time_calls(r8.append, args.steps)
+    kvb8 = kv_bytes_int8(wk)
+    del r8, rk
     torch.cuda.empty_cache()
 
     w5 = W.config(5)
@@ -558,6 +620,16 @@ def main(argv=None):
             "in_step_p90_us": round(pct(dec_ms, 90) * 1e3, 2),
             "copy_GBps": round(copy_gbs, 1),
             "frac_of_copy": round(achieved / copy_gbs, 4),
+        },
+        "int8_decode": {
+            "workload": "the same decode step over an INT8 cache (int8 codes, one float32 scale "
+                        "per token head row; random codes and scales)",
+            "bytes": kvb8,
+            "avg_us": round(i8_ms * 1e3, 2),
+            "GBps": round(kvb8 / (i8_ms / 1e3) / 1e9, 1),
+            "frac": round(kvb8 / (i8_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "speedup_vs_bf16": round(dec_avg_s * 1e3 / i8_ms, 3),
+            "append_avg_us": round(i8_app_ms * 1e3, 2),
         },
         "append": {
             "tokens": wk.T,

@@ -25,6 +25,8 @@ Printed as one JSON line:
              still match the ones it was taken on
   prefill    paged_prefill_attention on the mixed Qwen2.5-0.5B-shaped batch
              (4 prompts x 512 tokens, h_q=14, h_kv=2, d_h=64) in TFLOP/s
+  verify_decode  the chunked-prefill call with 4 new tokens per config-3
+             sequence (a speculative verify step), in KV GB/s
   int8_decode  paged_decode_attention_int8 on the same decode step over an
              INT8 cache: bytes = sum_b L_b * 2 * h_kv * (d_h + 4) (codes and
              one float32 scale per token head row), time over back-to-back
@@ -570,6 +572,18 @@ def main(argv=None):
     del r8, rk
     torch.cuda.empty_cache()
 
+    # multi-token decode (a speculative verify step): the 4 newest tokens of each
+    # config-3 sequence attend causally over its whole cache, through the
+    # chunked-prefill call
+    wv = W.build("verify", np.random.default_rng(274003), dtype="bf16", h_q=wk.h_q,
+                 h_kv=wk.h_kv, d=wk.d, decode_lens=[],
+                 prefill=[(int(L), 4) for L in wk.dec_context_lens], free_frac=0.1)
+    rv = Resident(wv, dev, copies=args.copies)
+    v_ms = time_calls(rv.prefill, args.steps, warmup=5)
+    kvbv = int(wv.pre_context_lens.to(torch.int64).sum()) * 2 * wv.h_kv * wv.d * wv.elem_bytes
+    del rv
+    torch.cuda.empty_cache()
+
     w5 = W.config(5)
     r5 = Resident(w5, dev)
     r5.append(0)
@@ -630,6 +644,14 @@ def main(argv=None):
             "frac": round(kvb8 / (i8_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "speedup_vs_bf16": round(dec_avg_s * 1e3 / i8_ms, 3),
             "append_avg_us": round(i8_app_ms * 1e3, 2),
+        },
+        "verify_decode": {
+            "workload": "multi-token decode: the 4 newest tokens of each of the 64 config-3 "
+                        "sequences attend causally over their caches (chunked-prefill call)",
+            "kv_bytes": kvbv,
+            "avg_us": round(v_ms * 1e3, 2),
+            "GBps": round(kvbv / (v_ms / 1e3) / 1e9, 1),
+            "frac": round(kvbv / (v_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         },
         "append": {
             "tokens": wk.T,

@@ -244,6 +244,27 @@ def test_prefill_grid(d, h_q, h_kv, seqs):
     check_prefill(w, res, kc_ref, vc_ref)
 
 
+@pytest.mark.parametrize("n_s", [2, 4, 5])
+def test_multi_token_decode_verify(n_s):
+    """Multi-token decode (a speculative verify step: the n_s newest tokens of
+    each sequence attend causally over its whole cache) runs as chunked prefill
+    with tiny n_s, on decode-shaped contexts; its last row equals a one-token
+    decode over the same context."""
+    rng = np.random.default_rng(40 + n_s)
+    lens = [int(x) for x in rng.integers(128, 4096, size=12, endpoint=True)] + [n_s, 16 + n_s]
+    w = W.build("verify", rng, dtype="bf16", h_q=32, h_kv=8, d=128,
+                prefill=[(L, n_s) for L in lens], free_frac=0.1, poison=True)
+    res = run(w, DEV)
+    kc_ref, vc_ref = check_append(w, res)
+    check_prefill(w, res, kc_ref, vc_ref)
+    last = w.pre_cu_seqlens[1:].long() - 1
+    q_last = w.pre_q[last]
+    one = ops.paged_decode_attention(q_last.to(DEV), res.k_cache.to(DEV), res.v_cache.to(DEV),
+                                     w.pre_block_tables.to(DEV), w.pre_context_lens.to(DEV),
+                                     max(lens), scale=w.scale).cpu()
+    assert max_err(res.prefill[last], one.double().numpy()) <= 2e-2
+
+
 @pytest.mark.parametrize("scale", [-0.2, 1.0])
 def test_negative_and_large_scale(scale):
     """Any finite scale: a negative one reverses the ranking of the keys, a

@@ -34,8 +34,8 @@ Printed as one JSON line:
   cpu_baseline  the CPU oracle on the same decode step, on one host core.
 
 Counter runs and their summaries (written to profiles/):
-  python bench.py --profile decode|prefill --steps N    short run for rocprofv3
-  python bench.py --summarize stats|traffic|mfma ...    rocprofv3 CSV -> profiles/*.txt
+  python bench.py --profile decode|decode_int8|prefill --steps N    short run for rocprofv3
+  python bench.py --summarize stats|traffic|traffic_int8|mfma ...   rocprofv3 CSV -> profiles/*.txt
 """
 from __future__ import annotations
 
@@ -374,8 +374,10 @@ def _calibration(ds, counter):
     return raw, COPY_BYTES / raw
 
 
-def summarize_traffic(k, fetch_csv, write_csv, steps, extra):
+def summarize_traffic(k, fetch_csv, write_csv, steps, extra, int8=False):
     w = W.config(k)
+    what = "decode_int8" if int8 else "decode"
+    call = "paged_decode_attention_int8" if int8 else "paged_decode_attention"
     f = _dispatches(fetch_csv)
     wr = _dispatches(write_csv)
     f_raw, f_fac = _calibration(f, "FETCH_SIZE")
@@ -391,23 +393,26 @@ def summarize_traffic(k, fetch_csv, write_csv, steps, extra):
         lines.append(f"#   {key:24s} FETCH_SIZE {fk:12.1f} KiB x {f_fac:.3f} = {fb / 1e6:9.3f} MB"
                      f"   WRITE_SIZE {wk:10.1f} KiB x {w_fac:.3f} = {wb / 1e6:8.3f} MB"
                      f"   ({n_f}/{n_w} dispatches)")
-    alg = kv_bytes(w)
+    alg = kv_bytes_int8(w) if int8 else kv_bytes(w)
+    over = " over an INT8 cache (codes + one float32 scale per token head row)" if int8 else ""
     text = [
-        f"# HBM traffic of one paged_decode_attention call ({WORKLOAD[k]})",
+        f"# HBM traffic of one {call} call ({WORKLOAD[k]}){over}",
         "# counters: rocprofv3 --pmc, one pass per counter, KiB per dispatch, averaged over the",
         "# decode dispatches; each scaled by what the same counter reads for a plain device copy",
         f"# of {COPY_BYTES} bytes in the same run (the largest *copy* dispatch).",
         "# commands (repository root, on the GPU):",
-        "#   " + CMD_PMC.format(counters="FETCH_SIZE", dir="pmc_fetch", what="decode", steps=steps,
-                                args=extra),
-        "#   " + CMD_PMC.format(counters="WRITE_SIZE", dir="pmc_write", what="decode", steps=steps,
-                                args=extra),
-        f"#   python bench.py --summarize traffic{extra} --steps {steps} "
-        "gpurun_out/pmc_fetch/run_counter_collection.csv gpurun_out/pmc_write/run_counter_collection.csv",
+        "#   " + CMD_PMC.format(counters="FETCH_SIZE", dir=f"pmc_fetch{'_i8' if int8 else ''}",
+                                what=what, steps=steps, args=extra),
+        "#   " + CMD_PMC.format(counters="WRITE_SIZE", dir=f"pmc_write{'_i8' if int8 else ''}",
+                                what=what, steps=steps, args=extra),
+        f"#   python bench.py --summarize {'traffic_int8' if int8 else 'traffic'}{extra} "
+        f"--steps {steps} gpurun_out/pmc_fetch{'_i8' if int8 else ''}/run_counter_collection.csv "
+        f"gpurun_out/pmc_write{'_i8' if int8 else ''}/run_counter_collection.csv",
         f"# calibration: copy FETCH_SIZE reads {f_raw / 1e6:.3f} MB -> factor {f_fac:.4f}; "
         f"WRITE_SIZE reads {w_raw / 1e6:.3f} MB -> factor {w_fac:.4f}",
         *lines,
-        f"# algorithmic KV bytes per call {alg}; measured read / algorithmic = {total_f / alg:.4f}",
+        f"# algorithmic {'INT8 ' if int8 else ''}KV bytes per call {alg}; measured read / algorithmic"
+        f" = {total_f / alg:.4f}",
         f"decode_sources_sha256: {digest(DECODE_SOURCES)}",
         f"fetch_bytes_per_call: {int(round(total_f))}",
         f"write_bytes_per_call: {int(round(total_w))}",
@@ -498,6 +503,10 @@ def profile_run(what: str, k: int, steps: int, dev: str):
         r = Resident(W.config(k), dev, copies=3)
         for i in range(steps):
             r.decode(i)
+    elif what == "decode_int8":
+        r8 = ResidentInt8(Resident(W.config(k), dev), copies=3)
+        for i in range(steps):
+            r8.decode(i)
     else:
         r = Resident(W.config(5), dev)
         r.append(0)
@@ -516,17 +525,19 @@ def main(argv=None):
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--cpu-reps", type=int, default=15)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile", choices=("decode", "prefill"))
-    ap.add_argument("--summarize", choices=("stats", "traffic", "mfma"))
+    ap.add_argument("--profile", choices=("decode", "decode_int8", "prefill"))
+    ap.add_argument("--summarize", choices=("stats", "traffic", "traffic_int8", "mfma"))
     ap.add_argument("inputs", nargs="*")
     args = ap.parse_args(argv)
     extra = "" if args.config == 3 else f" --config {args.config}"
 
     if args.summarize:
         os.makedirs(PROFILES, exist_ok=True)
-        if args.summarize == "traffic":
-            text = summarize_traffic(args.config, args.inputs[0], args.inputs[1], args.steps, extra)
-            path = summary_path(args.config, "hbm_traffic")
+        if args.summarize in ("traffic", "traffic_int8"):
+            int8 = args.summarize == "traffic_int8"
+            text = summarize_traffic(args.config, args.inputs[0], args.inputs[1], args.steps, extra,
+                                     int8=int8)
+            path = summary_path(args.config, "int8_hbm_traffic" if int8 else "hbm_traffic")
         elif args.summarize == "mfma":
             text = summarize_mfma(args.inputs[0], args.steps)
             path = summary_path(5, "mfma")

@@ -25,10 +25,14 @@
 //    combine kernel merges them with the exact log-sum-exp rule.
 //
 // Inside a wave
-//  * 8 adjacent lanes cover one token row (16-byte loads), so a load
-//    instruction reads 8 tokens x 128 contiguous bytes and a block takes two
-//    passes.  The next block's loads are in flight while the current one is used.
-//  * q.K partial sums are combined across the 8 lanes of a token by DPP row
+//  * kLPT adjacent lanes cover one token row with 16-byte loads (16 lanes for
+//    bf16 rows of 128 channels, 8 otherwise), so a load instruction reads
+//    64 / kLPT tokens and a block takes two or four passes.  The next block's
+//    loads are in flight while the current one is used.
+//  * An INT8 cache keeps the bf16 lane mapping with 8 code bytes per lane and
+//    token, widened exactly to bf16 in registers; the token's K scale
+//    multiplies its score and its V scale the softmax weight.
+//  * q.K partial sums are combined across the lanes of a token by DPP row
 //    permutations (no LDS).  bf16 products use v_dot2_f32_bf16; for P.V the
 //    two tokens a lane holds are paired so that one v_dot2 adds both
 //    (weights rounded to bf16, accumulation in fp32).  fp32 inputs use fp32 FMAs.
@@ -45,10 +49,6 @@
 namespace pkv {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
-#ifndef PKV_DECODE_DEPTH
-#define PKV_DECODE_DEPTH 2
-#endif
-constexpr int kDepth = PKV_DECODE_DEPTH;  // K/V blocks a wave holds in registers
 
 constexpr float kNegInf = -__builtin_huge_valf();
 

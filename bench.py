@@ -31,6 +31,9 @@ Printed as one JSON line:
              INT8 cache: bytes = sum_b L_b * 2 * h_kv * (d_h + 4) (codes and
              one float32 scale per token head row), time over back-to-back
              calls, and kv_append_int8 of the step's new tokens
+  blocks     copy_blocks (copy on write inside a device pool set) and
+             swap_blocks (device <-> pinned host pool sets) on decode-shaped
+             pools, with a plain torch copy to and from pinned memory beside
   cpu_baseline  the CPU oracle on the same decode step, on one host core.
 
 Counter runs and their summaries (written to profiles/):
@@ -280,6 +283,56 @@ def time_copy(dev: str, nbytes: int = 1 << 30, iters: int = 10):
     del src, dst
     torch.cuda.empty_cache()
     return 2 * nbytes / t / 1e9
+
+
+def time_blocks(dev: str, iters: int = 20):
+    """copy_blocks and swap_blocks on pools shaped like the decode batch's (bf16
+    K and V, h_kv=8, d_h=128: 32 KiB per block and pool).  Copy on write of 64
+    blocks (one per sequence) and of 1024 blocks inside a device pool set; swap
+    out of 512 blocks (one 8192-token sequence) to a pinned host pool set and
+    back in.  Rates count bytes read plus bytes written for the device copies
+    and the bytes moved over PCIe for the swaps; a plain torch copy of the same
+    bytes to and from pinned memory is timed beside them."""
+    rng = np.random.default_rng(274010)
+    n_dev, n_host, blk = 4096, 512, (8, 16, 128)
+    pools = [torch.randn((n_dev,) + blk, device=dev).to(torch.bfloat16) for _ in range(2)]
+    host = [torch.zeros((n_host,) + blk, dtype=torch.bfloat16).pin_memory() for _ in range(2)]
+    bb = 8 * 16 * 128 * 2
+    res = {"block_bytes_per_pool": bb}
+    for n in (64, 1024):
+        perm = rng.permutation(n_dev)
+        pairs = torch.from_numpy(np.stack([perm[n:2 * n], perm[:n]], 1).astype(np.int32)).to(dev)
+        cow = ops.bind_copy_blocks(pools, pairs)
+        ms = time_calls(lambda i: cow(), iters)
+        moved = n * 2 * bb * 2
+        res[f"cow_{n}_us"] = round(ms * 1e3, 2)
+        res[f"cow_{n}_GBps"] = round(moved / (ms / 1e3) / 1e9, 1)
+    out_pairs = torch.from_numpy(np.stack([rng.permutation(n_dev)[:n_host], np.arange(n_host)],
+                                          1).astype(np.int32)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([np.arange(n_host), rng.permutation(n_dev)[:n_host]],
+                                         1).astype(np.int32)).to(dev)
+    moved = n_host * 2 * bb
+    swap_out = ops.bind_swap_blocks(pools, host, out_pairs)
+    swap_in = ops.bind_swap_blocks(host, pools, in_pairs)
+    ms_out = time_calls(lambda i: swap_out(), iters)
+    ms_in = time_calls(lambda i: swap_in(), iters)
+    flat_d = pools[0][:n_host * 2].reshape(-1)
+    flat_h = torch.empty(flat_d.shape, dtype=flat_d.dtype).pin_memory()
+    ms_d2h = time_calls(lambda i: flat_h.copy_(flat_d, non_blocking=True), iters)
+    ms_h2d = time_calls(lambda i: flat_d.copy_(flat_h, non_blocking=True), iters)
+    res.update({
+        "swap_blocks": n_host,
+        "swap_bytes": moved,
+        "swap_out_us": round(ms_out * 1e3, 2),
+        "swap_out_GBps": round(moved / (ms_out / 1e3) / 1e9, 2),
+        "swap_in_us": round(ms_in * 1e3, 2),
+        "swap_in_GBps": round(moved / (ms_in / 1e3) / 1e9, 2),
+        "torch_d2h_GBps": round(moved / (ms_d2h / 1e3) / 1e9, 2),
+        "torch_h2d_GBps": round(moved / (ms_h2d / 1e3) / 1e9, 2),
+    })
+    del pools, host, flat_h
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w: W.Workload, reps: int):
@@ -605,6 +658,7 @@ def main(argv=None):
     torch.cuda.empty_cache()
 
     copy_gbs = time_copy(dev)
+    blocks = time_blocks(dev)
     traffic = measured_traffic(args.config)
     mfma = measured_mfma()
 
@@ -670,6 +724,7 @@ def main(argv=None):
             "avg_us": round(statistics.mean(app_ms) * 1e3, 2),
             "GBps": round(app_bytes / (statistics.mean(app_ms) / 1e3) / 1e9, 1),
         },
+        "blocks": blocks,
         "prefill": {
             "workload": "qwen2.5-0.5b-shaped prefill: 4 prompts x 512 tokens, h_q=14, h_kv=2, "
                         "d_h=64, causal, bf16",

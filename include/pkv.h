@@ -216,6 +216,53 @@ int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_
                             int n_blocks, int max_blocks_per_seq, float scale, int dtype,
                             void* stream);
 
+/*
+ * Block copies between KV pools.
+ *
+ * A pool set is the pools of one layer that share one block numbering: the K
+ * and V pools, plus k_scale and v_scale for the INT8 cache.  Block b of a pool
+ * whose blocks are block_bytes long is bytes [b * block_bytes, (b + 1) *
+ * block_bytes) from its base; the copies are whole blocks, bit for bit.
+ *
+ *   pools, src_pools, dst_pools, block_bytes : HOST arrays of n_pools entries,
+ *       1 <= n_pools <= 8.  Each pool pointer is 16-byte aligned memory the GPU
+ *       can reach: device memory, or (swap_blocks) pinned host memory from
+ *       hipHostMalloc, which the kernel reads or writes through its device
+ *       mapping over PCIe.  Pageable host memory returns PKV_ERR_INVALID_ARG.
+ *       block_bytes[i] > 0, a multiple of 16, the same for source and
+ *       destination pool i.
+ *   pairs : int32 [n_pairs, 2] of (source block, destination block), device
+ *       memory or pinned host memory.  n_pairs == 0 enqueues nothing.  A pair
+ *       with an index outside [0, n_blocks) is skipped (and rejected under
+ *       PKV_DEBUG=1, as is a destination named twice).
+ * The pointer checks query the runtime (hipPointerGetAttributes) but enqueue
+ * nothing; the copy is one kernel on stream.
+ */
+
+/*
+ * copy_blocks - within one pool set, block dst of every pool becomes a copy of
+ * block src: the copy on write of a shared, partly filled block before a
+ * sequence appends into it (LLM Inference Server page, Stage 1 "KV-Cache
+ * Engine", prefix-cache task: sequences with the same system prompt share its
+ * blocks).  n_blocks: blocks of each pool.  No block may be both a source and
+ * a destination in one call (the copies run in parallel).
+ */
+int copy_blocks(void* const* pools, const int64_t* block_bytes, int n_pools, int n_blocks,
+                const int32_t* pairs, int n_pairs, void* stream);
+
+/*
+ * swap_blocks - between two pool sets (device and pinned host, either way, or
+ * two device sets): block dst of dst_pools[i] becomes a copy of block src of
+ * src_pools[i].  This moves a preempted sequence's blocks out of HBM and back
+ * in (the scheduler's preemption in the pipeline figure of the From Scratch
+ * page, How it works).  n_src_blocks, n_dst_blocks: blocks of each source and
+ * destination pool.  src_pools[i] == dst_pools[i] returns PKV_ERR_INVALID_ARG
+ * (use copy_blocks within one set); the two sets must not overlap.
+ */
+int swap_blocks(const void* const* src_pools, void* const* dst_pools, const int64_t* block_bytes,
+                int n_pools, int n_src_blocks, int n_dst_blocks, const int32_t* pairs,
+                int n_pairs, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t strea
   dst.resize(n);
   if (n == 0) return true;
   if (hipStreamSynchronize(stream) != hipSuccess) return false;
-  return hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost) == hipSuccess;
+  return hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDefault) == hipSuccess;
 }
 
 // PKV_DEBUG: context lengths and the block-table entries they reach.
@@ -65,6 +65,93 @@ int debug_check_slots(const int64_t* slot_mapping, int T, int n_blocks, hipStrea
     seen[(size_t)v] = 1;
   }
   return PKV_OK;
+}
+
+// Device address of a pool the GPU can reach: device or managed memory as is,
+// pinned host memory through its device mapping.  False for memory the GPU
+// cannot reach (pageable host memory, unknown pointers); the runtime's error is
+// cleared so that it is not reported by a later launch check.
+bool device_address(const void* p, const void** out) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) {
+    *out = p;
+    return true;
+  }
+  if (a.type == hipMemoryTypeHost) {
+    // Only memory the runtime pinned (hipHostMalloc or registered) has flags
+    // and a device mapping.
+    unsigned int flags = 0;
+    void* d = nullptr;
+    if (hipHostGetFlags(&flags, const_cast<void*>(p)) != hipSuccess ||
+        hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess || !d) {
+      (void)hipGetLastError();
+      return false;
+    }
+    *out = d;
+    return true;
+  }
+  return false;
+}
+
+// PKV_DEBUG: block pairs in range, no destination named twice and, within one
+// pool set, no block both read and written.
+int debug_check_pairs(const int32_t* pairs, int n_pairs, int n_src, int n_dst, bool same_set,
+                      hipStream_t stream) {
+  std::vector<int32_t> p;
+  if (!copy_to_host(p, pairs, (size_t)n_pairs * 2, stream)) return PKV_ERR_HIP;
+  std::vector<char> written((size_t)n_dst, 0), read(same_set ? (size_t)n_src : 0, 0);
+  for (int i = 0; i < n_pairs; ++i) {
+    const int32_t s = p[2 * (size_t)i], d = p[2 * (size_t)i + 1];
+    if (s < 0 || s >= n_src || d < 0 || d >= n_dst || written[(size_t)d]) return PKV_ERR_INVALID_ARG;
+    written[(size_t)d] = 1;
+    if (same_set) read[(size_t)s] = 1;
+  }
+  if (same_set)
+    for (int b = 0; b < n_src; ++b)
+      if (read[(size_t)b] && written[(size_t)b]) return PKV_ERR_INVALID_ARG;
+  return PKV_OK;
+}
+
+// Both block-copy entry points.  src == dst for a copy within one pool set.
+int copy_call(const void* const* src, void* const* dst, const int64_t* block_bytes, int n_pools,
+              int n_src, int n_dst, const int32_t* pairs, int n_pairs, bool same_set,
+              void* stream) {
+  if (n_pools < 1 || n_pools > pkv::kMaxCopyPools || n_src < 1 || n_dst < 1 || n_pairs < 0 ||
+      !src || !dst || !block_bytes)
+    return PKV_ERR_INVALID_ARG;
+  for (int i = 0; i < n_pools; ++i) {
+    const int64_t bb = block_bytes[i];
+    if (bb <= 0 || (bb & 15) || !src[i] || !dst[i] || !aligned16(src[i]) || !aligned16(dst[i]))
+      return PKV_ERR_INVALID_ARG;
+    if (!same_set && src[i] == dst[i]) return PKV_ERR_INVALID_ARG;
+    if (bb / 16 > (int64_t)65535 * 2048) return PKV_ERR_UNSUPPORTED;
+  }
+  if (n_pairs == 0) return PKV_OK;
+  if (!pairs || ((uintptr_t)pairs & 3u)) return PKV_ERR_INVALID_ARG;
+  pkv::CopyPools p;
+  memset(&p, 0, sizeof(p));
+  for (int i = 0; i < n_pools; ++i) {
+    const void* s_dev;
+    const void* d_dev;
+    if (!device_address(src[i], &s_dev) || !device_address(dst[i], &d_dev))
+      return PKV_ERR_INVALID_ARG;
+    p.src[i] = (const uint4*)s_dev;
+    p.dst[i] = (uint4*)d_dev;
+    p.vecs[i] = block_bytes[i] / 16;
+  }
+  const void* pairs_dev;
+  if (!device_address(pairs, &pairs_dev)) return PKV_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (debug_checks()) {
+    const int rc = debug_check_pairs(pairs, n_pairs, n_src, n_dst, same_set, s);
+    if (rc != PKV_OK) return rc;
+  }
+  return from_hip(pkv::launch_copy_blocks(p, n_pools, (const int32_t*)pairs_dev, n_pairs, n_src,
+                                          n_dst, s));
 }
 
 // Pool element type of a decode dtype code; false for an unknown code.
@@ -305,6 +392,19 @@ int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.scale_log2 = scale * kLog2e;
   return from_hip(pkv::launch_prefill_bf16(a, d_h, s));
+}
+
+int copy_blocks(void* const* pools, const int64_t* block_bytes, int n_pools, int n_blocks,
+                const int32_t* pairs, int n_pairs, void* stream) {
+  return copy_call((const void* const*)pools, pools, block_bytes, n_pools, n_blocks, n_blocks,
+                   pairs, n_pairs, true, stream);
+}
+
+int swap_blocks(const void* const* src_pools, void* const* dst_pools, const int64_t* block_bytes,
+                int n_pools, int n_src_blocks, int n_dst_blocks, const int32_t* pairs,
+                int n_pairs, void* stream) {
+  return copy_call(src_pools, dst_pools, block_bytes, n_pools, n_src_blocks, n_dst_blocks, pairs,
+                   n_pairs, false, stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,64 @@
+// copy_blocks / swap_blocks: whole physical blocks copied between pools.
+//
+// Within one pool set this is the copy that a shared, partly filled block needs
+// before one of its sequences writes into it (the prefix cache of the LLM
+// Inference Server page, Stage 1: sequences with the same system prompt share
+// its blocks).  Between a device pool set and a pinned host pool set it moves a
+// preempted sequence's blocks out of HBM and back (the scheduler's preemption
+// in the pipeline figure of the From Scratch page, How it works).
+//
+// A pool is any array whose leading axis is the physical block; block b of pool
+// i is bytes [b * block_bytes[i], (b + 1) * block_bytes[i]).  One workgroup
+// moves one 32 KiB slice of one block of one pool: each lane issues its eight
+// 16-byte loads before any store, so a wave keeps 8 KiB in flight, and the
+// slices of a block are coalesced runs.  Host pools are reached through their
+// device mapping (pinned memory), so a swap is one launch over PCIe whatever
+// the number of blocks, not one DMA request per block.
+#include "device_common.h"
+#include "launch.h"
+
+namespace pkv {
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 8;
+constexpr int kCopySliceVecs = kCopyThreads * kCopyUnroll;  // 2048 vectors = 32 KiB
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    CopyPools p, const int32_t* __restrict__ pairs, int n_src_blocks, int n_dst_blocks) {
+  const int pool = blockIdx.y;
+  const int64_t vecs = p.vecs[pool];
+  const int64_t first = (int64_t)blockIdx.z * kCopySliceVecs;
+  if (first >= vecs) return;
+  const int32_t src = pairs[2 * (int64_t)blockIdx.x];
+  const int32_t dst = pairs[2 * (int64_t)blockIdx.x + 1];
+  if (src < 0 || src >= n_src_blocks || dst < 0 || dst >= n_dst_blocks) return;
+  const uint4* __restrict__ s = p.src[pool] + (int64_t)src * vecs + first;
+  uint4* __restrict__ d = p.dst[pool] + (int64_t)dst * vecs + first;
+  const int64_t n = vecs - first < kCopySliceVecs ? vecs - first : kCopySliceVecs;
+  uint4 r[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = (int64_t)u * kCopyThreads + threadIdx.x;
+    if (i < n) r[u] = s[i];
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = (int64_t)u * kCopyThreads + threadIdx.x;
+    if (i < n) d[i] = r[u];
+  }
+}
+
+hipError_t launch_copy_blocks(const CopyPools& p, int n_pools, const int32_t* pairs, int n_pairs,
+                              int n_src_blocks, int n_dst_blocks, hipStream_t stream) {
+  int64_t most = 0;
+  for (int i = 0; i < n_pools; ++i) most = p.vecs[i] > most ? p.vecs[i] : most;
+  const int64_t slices = (most + kCopySliceVecs - 1) / kCopySliceVecs;
+  if (n_pairs <= 0 || n_pools <= 0 || slices <= 0) return hipSuccess;
+  if (slices > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)n_pairs, (unsigned)n_pools,
+                                              (unsigned)slices),
+                     dim3(kCopyThreads), 0, stream, p, pairs, n_src_blocks, n_dst_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

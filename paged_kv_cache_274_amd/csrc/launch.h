@@ -116,4 +116,21 @@ struct PrefillArgs {
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d_h, hipStream_t stream);
 
+// Block copies between pool sets: up to kMaxCopyPools pools (K, V, and for the
+// INT8 cache their scales) share one block mapping.  src/dst are device
+// addresses (a pinned host pool's device mapping included); vecs[i] is the
+// 16-byte vectors per block of pool i.
+constexpr int kMaxCopyPools = 8;
+struct CopyPools {
+  const uint4* src[kMaxCopyPools];
+  uint4* dst[kMaxCopyPools];
+  int64_t vecs[kMaxCopyPools];
+};
+
+// pairs: int32 [n_pairs][2] (source block, destination block), device-visible.
+// A pair with an index out of range is skipped.  Returns hipErrorInvalidValue
+// when a block is too large for the grid (more than 65535 slices of 32 KiB).
+hipError_t launch_copy_blocks(const CopyPools& p, int n_pools, const int32_t* pairs, int n_pairs,
+                              int n_src_blocks, int n_dst_blocks, hipStream_t stream);
+
 }  // namespace pkv

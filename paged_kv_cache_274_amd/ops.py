@@ -22,7 +22,8 @@ _DTYPE = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
 _WS_DTYPE = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.int8: PKV_INT8}
 EXPORTED = ("kv_append", "paged_decode_attention", "paged_prefill_attention",
             "kv_append_int8", "paged_decode_attention_int8",
-            "pkv_decode_workspace_bytes", "pkv_decode_num_splits", "pkv_status_string")
+            "pkv_decode_workspace_bytes", "pkv_decode_num_splits", "pkv_status_string",
+            "copy_blocks", "swap_blocks")
 
 _lib = None
 
@@ -63,6 +64,12 @@ def lib() -> ctypes.CDLL:
                                               i32, i32, i32, i32, ctypes.c_float, i32, vp,
                                               ctypes.c_size_t, vp]
     L.paged_decode_attention_int8.restype = i32
+    ptrs = ctypes.POINTER(ctypes.c_void_p)
+    sizes = ctypes.POINTER(ctypes.c_int64)
+    L.copy_blocks.argtypes = [ptrs, sizes, i32, i32, i32p, i32, vp]
+    L.copy_blocks.restype = i32
+    L.swap_blocks.argtypes = [ptrs, ptrs, sizes, i32, i32, i32, i32p, i32, vp]
+    L.swap_blocks.restype = i32
     _lib = L
     return L
 
@@ -273,4 +280,89 @@ def bind_prefill(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache: torch.Ten
         if rc != 0:
             raise PkvError("paged_prefill_attention", rc)
         return out
+    return call
+
+
+MAX_COPY_POOLS = 8
+
+
+def _pool_set(pools, what: str):
+    """(n_blocks, block bytes of each pool) of a pool set: tensors whose leading
+    axis is the physical block."""
+    _need(1 <= len(pools) <= MAX_COPY_POOLS, f"{what}: 1..{MAX_COPY_POOLS} pools")
+    n_blocks = int(pools[0].shape[0])
+    sizes = []
+    for t in pools:
+        _need(t.dim() >= 1 and int(t.shape[0]) == n_blocks,
+              f"{what}: every pool needs the same number of blocks")
+        _need(t.is_contiguous(), f"{what}: pools must be contiguous")
+        _need(t.is_cuda or t.is_pinned(), f"{what}: pools must be on the GPU or in pinned memory")
+        sizes.append(t.numel() * t.element_size() // n_blocks if n_blocks else 0)
+    return n_blocks, sizes
+
+
+def _pairs(pairs: torch.Tensor) -> int:
+    _need(pairs.dtype == torch.int32 and pairs.dim() == 2 and pairs.shape[1] == 2 and
+          pairs.is_contiguous(), "pairs must be contiguous int32 [n, 2] of (src, dst) blocks")
+    _need(pairs.is_cuda or pairs.is_pinned(), "pairs must be on the GPU or in pinned memory")
+    return int(pairs.shape[0])
+
+
+def _copy_stream(tensors) -> int:
+    for t in tensors:
+        if t.is_cuda:
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return torch.cuda.current_stream().cuda_stream
+
+
+def copy_blocks(pools, pairs: torch.Tensor) -> None:
+    """Within one pool set (e.g. [k_cache, v_cache], plus the scale pools of an
+    INT8 cache), block dst of every pool becomes a copy of block src, for every
+    (src, dst) row of pairs (int32 [n, 2])."""
+    bind_copy_blocks(pools, pairs)()
+
+
+def bind_copy_blocks(pools, pairs: torch.Tensor):
+    """copy_blocks with its arguments checked and marshalled once: returns a
+    call that launches it (on the stream current now)."""
+    n_blocks, sizes = _pool_set(pools, "pools")
+    n = _pairs(pairs)
+    ptr = (ctypes.c_void_p * len(pools))(*[t.data_ptr() for t in pools])
+    bb = (ctypes.c_int64 * len(pools))(*sizes)
+    fn = lib().copy_blocks
+    args = (ptr, bb, len(pools), n_blocks, pairs.data_ptr(), n, _copy_stream([*pools, pairs]))
+
+    def call() -> None:
+        rc = fn(*args)
+        if rc != 0:
+            raise PkvError("copy_blocks", rc)
+    return call
+
+
+def swap_blocks(src_pools, dst_pools, pairs: torch.Tensor) -> None:
+    """Between two pool sets (GPU and pinned host, either way): block dst of
+    dst_pools[i] becomes a copy of block src of src_pools[i]."""
+    bind_swap_blocks(src_pools, dst_pools, pairs)()
+
+
+def bind_swap_blocks(src_pools, dst_pools, pairs: torch.Tensor):
+    """swap_blocks with its arguments checked and marshalled once."""
+    _need(len(src_pools) == len(dst_pools), "pool sets differ in length")
+    n_src, s_sizes = _pool_set(src_pools, "src_pools")
+    n_dst, d_sizes = _pool_set(dst_pools, "dst_pools")
+    for s, d in zip(src_pools, dst_pools):
+        _need(s.shape[1:] == d.shape[1:] and s.dtype == d.dtype,
+              "a source and a destination pool differ in block shape or dtype")
+    n = _pairs(pairs)
+    sp = (ctypes.c_void_p * len(src_pools))(*[t.data_ptr() for t in src_pools])
+    dp = (ctypes.c_void_p * len(dst_pools))(*[t.data_ptr() for t in dst_pools])
+    bb = (ctypes.c_int64 * len(src_pools))(*s_sizes)
+    fn = lib().swap_blocks
+    args = (sp, dp, bb, len(src_pools), n_src, n_dst, pairs.data_ptr(), n,
+            _copy_stream([*src_pools, *dst_pools, pairs]))
+
+    def call() -> None:
+        rc = fn(*args)
+        if rc != 0:
+            raise PkvError("swap_blocks", rc)
     return call

@@ -169,3 +169,50 @@ def test_decode_int8_validation():
                 ops.decode_workspace_bytes(4, 8, 2, 128, 256, torch.bfloat16, n))
     assert ops.lib().paged_decode_attention(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 2, 128, 64,
                                             16, 256, 0.1, 2, 0, FAKE, 1 << 30, None) == 1
+
+
+def _ptrs(*vals):
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+def _sizes(*vals):
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+def _copy(pools=(FAKE, FAKE), sizes=(4096, 4096), n_pools=None, nb=8, pairs=FAKE, n=4):
+    n_pools = len(pools) if n_pools is None else n_pools
+    return ops.lib().copy_blocks(_ptrs(*pools), _sizes(*sizes), n_pools, nb, pairs, n, None)
+
+
+def _swap(src=(FAKE, FAKE), dst=(FAKE + 64, FAKE + 64), sizes=(4096, 4096), n_pools=None,
+          ns=8, nd=4, pairs=FAKE, n=4):
+    n_pools = len(src) if n_pools is None else n_pools
+    return ops.lib().swap_blocks(_ptrs(*src), _ptrs(*dst), _sizes(*sizes), n_pools, ns, nd, pairs,
+                                 n, None)
+
+
+def test_copy_blocks_validation():
+    """Every error here is found before the library asks the runtime anything."""
+    assert _copy(n_pools=0) == 1
+    assert _copy(pools=(FAKE,) * 9, sizes=(4096,) * 9) == 1
+    assert _copy(nb=0) == 1
+    assert _copy(n=-1) == 1
+    assert _copy(sizes=(4096, 0)) == 1
+    assert _copy(sizes=(4096, 4104)) == 1          # not a multiple of 16
+    assert _copy(pools=(FAKE, None)) == 1
+    assert _copy(pools=(FAKE, MISALIGNED)) == 1
+    assert _copy(sizes=(4096, 16 * 65535 * 2048 + 16)) == 2   # more slices than a grid holds
+    assert _copy(pairs=None) == 1
+    assert _copy(pairs=FAKE + 2) == 1
+    assert _copy(n=0, pairs=None) == 0              # empty: nothing enqueued
+    assert ops.lib().copy_blocks(None, _sizes(16), 1, 8, FAKE, 1, None) == 1
+
+
+def test_swap_blocks_validation():
+    assert _swap(ns=0) == 1
+    assert _swap(nd=0) == 1
+    assert _swap(dst=(FAKE, FAKE + 64)) == 1        # a pool copied onto itself
+    assert _swap(dst=(FAKE + 64, MISALIGNED)) == 1
+    assert _swap(sizes=(4096, 24)) == 1
+    assert _swap(pairs=FAKE + 1) == 1
+    assert _swap(n=0, pairs=None) == 0

@@ -64,7 +64,8 @@ typedef enum {
   PKV_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad device value (PKV_DEBUG) */
   PKV_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (d_h, dtype) */
   PKV_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
-  PKV_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+  PKV_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  PKV_ERR_NO_BLOCKS = 5    /* block manager: not enough free blocks; nothing changed */
 } pkv_status;
 
 /* Human-readable name of a status code (static storage). */
@@ -262,6 +263,115 @@ int copy_blocks(void* const* pools, const int64_t* block_bytes, int n_pools, int
 int swap_blocks(const void* const* src_pools, void* const* dst_pools, const int64_t* block_bytes,
                 int n_pools, int n_src_blocks, int n_dst_blocks, const int32_t* pairs,
                 int n_pairs, void* stream);
+
+/*
+ * Block manager (host-only; no HIP call).  It decides which physical block of a
+ * pool holds each token of each sequence: the block tables and slots that the
+ * calls above take.  It is the block pool with per-sequence block tables of
+ * the LLM Inference Server page (Optional Stretch Challenges, "Paged KV-Cache
+ * Block Allocator"), with blocks shared across requests (Mini inference engine
+ * page, section 2), the hash-keyed prefix cache with hit/miss counts whose
+ * second request sharing a system prompt skips prefill on it (LLM Inference
+ * Server page, Stage 1 "KV-Cache Engine", prefix-cache task; From Scratch page,
+ * "Take it further"), a fixed budget that rejects what does not fit so the
+ * caller can queue it (Stage 1, footprint-calculator task), and swapping of
+ * preempted sequences (the preempt/swap of the Scheduler box, pipeline figure,
+ * From Scratch page).  The device memory itself stays the caller's: the
+ * manager returns the copies to make, and the caller runs copy_blocks /
+ * swap_blocks BEFORE the kv_append of the same step.
+ *
+ * Policy:
+ *   - Free blocks form one FIFO queue, initially 0..n_blocks-1.  Allocation
+ *     takes the head; a block whose last holder lets go joins the tail; a freed
+ *     sequence lets go of its blocks last block first.
+ *   - With prefix_cache != 0, every block that holds tokens stays indexed by
+ *     (the tokens before it, the tokens it holds) until it is reallocated, held
+ *     or not.  A new prompt is matched block by block: among the indexed
+ *     blocks with the same preceding tokens, the one sharing the longest run of
+ *     leading tokens with the prompt's block (ties: the lowest id).  A whole
+ *     16-token match continues with the next block, a shorter one ends the
+ *     match; the matched tokens are reported as cached.  The position key is a
+ *     64-bit hash chain over the preceding full blocks (the block's own tokens
+ *     are compared exactly).
+ *   - Writing a token at offset o of a block another sequence also holds
+ *     copies it first to a new block (copy on write: one (src, dst) pair).  A
+ *     block held alone that holds more than o tokens drops them and is written
+ *     in place.  A copy's source is always still held, so the pairs of one step
+ *     never name a block both as a source and as a destination.
+ *   - Operations are all or nothing: one that needs more free blocks than
+ *     there are returns PKV_ERR_NO_BLOCKS and changes nothing.
+ *   - Swap out copies every block of a sequence to host blocks (a FIFO queue
+ *     of n_host_blocks of its own) and lets go of the device blocks; swap in
+ *     allocates new device blocks and frees the host blocks.
+ * A manager is not thread-safe; calls on one handle must not overlap.
+ * Sequence ids are the caller's (any int64); an unknown, swapped (where not
+ * allowed) or duplicate id returns PKV_ERR_INVALID_ARG.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+typedef struct {
+  int32_t n_blocks, free_blocks;
+  int32_t cached_blocks;       /* blocks indexed by the prefix cache, held or free */
+  int32_t cached_free_blocks;  /* of those, the ones no sequence holds */
+  int32_t n_host_blocks, host_free_blocks, n_sequences;
+  int64_t hit_tokens, query_tokens;   /* prompt tokens served from the cache / looked up */
+  int64_t hit_requests, requests;     /* prompts with at least one cached token / all */
+} pkv_bm_stats;
+
+/* A manager of n_blocks >= 1 device blocks and n_host_blocks >= 0 host blocks;
+ * NULL on invalid sizes or out of memory.  Destroy frees it (NULL is a no-op). */
+pkv_block_manager* pkv_bm_create(int n_blocks, int n_host_blocks, int prefix_cache);
+void pkv_bm_destroy(pkv_block_manager* bm);
+
+/* Admit a prompt of n_tokens token ids (host int32).  Outputs (host):
+ *   slots[n_tokens] : the slot of each token, -1 for the *n_cached leading
+ *                     tokens already in the pool (kv_append skips negative
+ *                     slots, and the prefill runs the last n_tokens - *n_cached
+ *                     tokens as a chunked prefill);
+ *   cow_pairs[2], *n_cow : at most one copy on write to run first.
+ * PKV_ERR_NO_BLOCKS when the pool cannot hold it (nothing changes). */
+int pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens,
+                        int n_tokens, int64_t* slots, int32_t* cow_pairs, int* n_cow,
+                        int* n_cached);
+
+/* Append n_tokens tokens (a decode step: one; a verify step: a few) to a
+ * sequence; slots[n_tokens] and at most one copy on write as above. */
+int pkv_bm_append(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens, int n_tokens,
+                  int64_t* slots, int32_t* cow_pairs, int* n_cow);
+
+/* child shares every block of parent (parallel sampling); later writes copy on
+ * write. */
+int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
+
+/* Lets go of a sequence's blocks (device or host). */
+int pkv_bm_free(pkv_block_manager* bm, int64_t seq_id);
+
+/* Swap a sequence out (pairs = (device block, host block)) or in (pairs =
+ * (host block, device block)); pairs has room for max_pairs pairs, one per
+ * block of the sequence.  Run swap_blocks on them before the next step. */
+int pkv_bm_swap_out(pkv_block_manager* bm, int64_t seq_id, int32_t* pairs, int max_pairs,
+                    int* n_pairs);
+int pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq_id, int32_t* pairs, int max_pairs,
+                   int* n_pairs);
+
+/* A resident sequence's block table (host int32, room for max_blocks) and its
+ * length.  *n_blocks and *seq_len are set for any known sequence, also when
+ * max_blocks is too small or the sequence is swapped out (both return
+ * PKV_ERR_INVALID_ARG). */
+int pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq_id, int32_t* table,
+                       int max_blocks, int* n_blocks, int* seq_len);
+
+int pkv_bm_get_stats(const pkv_block_manager* bm, pkv_bm_stats* out);
+
+/* KV-cache bytes of batch sequences of seq_len tokens: the footprint
+ * 2 * n_layers * n_kv_heads * d_head * seq_len * bytes_per_elem of the LLM
+ * Inference Server page (Required Mathematical Concepts; its
+ * compute_kv_cache_bytes task), times batch.  dtype PKV_F32 / PKV_BF16, or
+ * PKV_INT8 (one byte per element plus one float32 scale per token head row).
+ * paged != 0 rounds each sequence up to whole 16-token blocks.  -1 on invalid
+ * arguments. */
+int64_t pkv_kv_cache_bytes(int n_layers, int h_kv, int d_h, int64_t batch, int64_t seq_len,
+                           int dtype, int paged);
 
 #ifdef __cplusplus
 }

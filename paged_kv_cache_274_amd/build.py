@@ -2,8 +2,9 @@
 
     python -m paged_kv_cache_274_amd.build
 
-Compiles every ``csrc/*.hip`` with hipcc for ``--offload-arch=gfx950`` in
-parallel and links them into ``paged_kv_cache_274_amd/libpkv.so``.  Packed
+Compiles every ``csrc/*.hip`` with hipcc for ``--offload-arch=gfx950`` and
+every host-only ``csrc/*.cpp`` with g++, in parallel, and links them into
+``paged_kv_cache_274_amd/libpkv.so``.  Packed
 fp32 instructions are disabled (``-packed-fp32-ops``): all fp32 math is scalar
 VALU code.
 """
@@ -31,16 +32,25 @@ CFLAGS = [
 ]
 
 
+CXX = os.environ.get("CXX", shutil.which("g++") or "g++")
+HOST_CFLAGS = ["-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-Wall", "-Wextra"]
+
+
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    """HIP sources (device kernels and their launchers) and host-only C++."""
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith(".hip") or f.endswith(".cpp"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [CXX, *HOST_CFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"compile failed on {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 

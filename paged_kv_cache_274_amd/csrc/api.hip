@@ -176,6 +176,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
     case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
     case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    case PKV_ERR_NO_BLOCKS: return "PKV_ERR_NO_BLOCKS";
   }
   return "PKV_UNKNOWN_STATUS";
 }

@@ -12,6 +12,7 @@ import math
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -23,7 +24,11 @@ _WS_DTYPE = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.int8: PKV_I
 EXPORTED = ("kv_append", "paged_decode_attention", "paged_prefill_attention",
             "kv_append_int8", "paged_decode_attention_int8",
             "pkv_decode_workspace_bytes", "pkv_decode_num_splits", "pkv_status_string",
-            "copy_blocks", "swap_blocks")
+            "copy_blocks", "swap_blocks",
+            "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_sequence", "pkv_bm_append",
+            "pkv_bm_fork", "pkv_bm_free", "pkv_bm_swap_out", "pkv_bm_swap_in",
+            "pkv_bm_block_table", "pkv_bm_get_stats", "pkv_kv_cache_bytes")
+PKV_ERR_NO_BLOCKS = 5
 
 _lib = None
 
@@ -32,6 +37,19 @@ class PkvError(RuntimeError):
     def __init__(self, what: str, status: int):
         super().__init__(f"{what} failed: {status_string(status)} ({status})")
         self.status = status
+
+
+class NoBlocksError(PkvError):
+    """The block manager has too few free blocks; nothing changed."""
+
+
+class BlockManagerStats(ctypes.Structure):
+    _fields_ = [("n_blocks", ctypes.c_int32), ("free_blocks", ctypes.c_int32),
+                ("cached_blocks", ctypes.c_int32), ("cached_free_blocks", ctypes.c_int32),
+                ("n_host_blocks", ctypes.c_int32), ("host_free_blocks", ctypes.c_int32),
+                ("n_sequences", ctypes.c_int32), ("hit_tokens", ctypes.c_int64),
+                ("query_tokens", ctypes.c_int64), ("hit_requests", ctypes.c_int64),
+                ("requests", ctypes.c_int64)]
 
 
 def lib() -> ctypes.CDLL:
@@ -70,6 +88,25 @@ def lib() -> ctypes.CDLL:
     L.copy_blocks.restype = i32
     L.swap_blocks.argtypes = [ptrs, ptrs, sizes, i32, i32, i32, i32p, i32, vp]
     L.swap_blocks.restype = i32
+    ip = ctypes.POINTER(ctypes.c_int)
+    i64 = ctypes.c_int64
+    L.pkv_bm_create.argtypes = [i32, i32, i32]
+    L.pkv_bm_create.restype = vp
+    L.pkv_bm_destroy.argtypes = [vp]
+    L.pkv_bm_destroy.restype = None
+    L.pkv_bm_add_sequence.argtypes = [vp, i64, vp, i32, vp, vp, ip, ip]
+    L.pkv_bm_append.argtypes = [vp, i64, vp, i32, vp, vp, ip]
+    L.pkv_bm_fork.argtypes = [vp, i64, i64]
+    L.pkv_bm_free.argtypes = [vp, i64]
+    L.pkv_bm_swap_out.argtypes = [vp, i64, vp, i32, ip]
+    L.pkv_bm_swap_in.argtypes = [vp, i64, vp, i32, ip]
+    L.pkv_bm_block_table.argtypes = [vp, i64, vp, i32, ip, ip]
+    L.pkv_bm_get_stats.argtypes = [vp, ctypes.POINTER(BlockManagerStats)]
+    for f in ("pkv_bm_add_sequence", "pkv_bm_append", "pkv_bm_fork", "pkv_bm_free",
+              "pkv_bm_swap_out", "pkv_bm_swap_in", "pkv_bm_block_table", "pkv_bm_get_stats"):
+        getattr(L, f).restype = i32
+    L.pkv_kv_cache_bytes.argtypes = [i32, i32, i32, i64, i64, i32, i32]
+    L.pkv_kv_cache_bytes.restype = i64
     _lib = L
     return L
 
@@ -366,3 +403,105 @@ def bind_swap_blocks(src_pools, dst_pools, pairs: torch.Tensor):
         if rc != 0:
             raise PkvError("swap_blocks", rc)
     return call
+
+
+def kv_cache_bytes(n_layers: int, h_kv: int, d_h: int, batch: int, seq_len: int,
+                   dtype: torch.dtype = torch.bfloat16, paged: bool = False) -> int:
+    """KV-cache footprint in bytes (torch.int8: the INT8 cache with its scales)."""
+    r = lib().pkv_kv_cache_bytes(n_layers, h_kv, d_h, batch, seq_len, _WS_DTYPE[dtype],
+                                 int(paged))
+    if r < 0:
+        raise ValueError("invalid kv_cache_bytes arguments")
+    return int(r)
+
+
+class BlockManager:
+    """The library's block manager (host-only C++): block tables, slots, prefix
+    cache, copy on write and swap plans.  Token ids are int32; slots come back
+    as int64 arrays ready for kv_append (-1 = already cached), copy pairs as
+    int32 [n, 2] arrays ready for copy_blocks / swap_blocks."""
+
+    def __init__(self, n_blocks: int, n_host_blocks: int = 0, prefix_cache: bool = True):
+        self._L = lib()
+        self._h = self._L.pkv_bm_create(int(n_blocks), int(n_host_blocks), int(prefix_cache))
+        if not self._h:
+            raise ValueError("pkv_bm_create: invalid sizes or out of memory")
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            self._L.pkv_bm_destroy(h)
+
+    def _check(self, what: str, rc: int):
+        if rc == PKV_ERR_NO_BLOCKS:
+            raise NoBlocksError(what, rc)
+        if rc != 0:
+            raise PkvError(what, rc)
+
+    @staticmethod
+    def _tokens(tokens) -> np.ndarray:
+        return np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+
+    def add_sequence(self, seq_id: int, tokens):
+        """-> (n_cached, slots int64 [n], cow_pairs int32 [0 or 1, 2])"""
+        t = self._tokens(tokens)
+        slots = np.empty(len(t), np.int64)
+        cow = np.empty((1, 2), np.int32)
+        n_cow, n_cached = ctypes.c_int(0), ctypes.c_int(0)
+        self._check("pkv_bm_add_sequence", self._L.pkv_bm_add_sequence(
+            self._h, int(seq_id), t.ctypes.data, len(t), slots.ctypes.data, cow.ctypes.data,
+            ctypes.byref(n_cow), ctypes.byref(n_cached)))
+        return n_cached.value, slots, cow[:n_cow.value].copy()
+
+    def append(self, seq_id: int, tokens):
+        """-> (slots int64 [n], cow_pairs int32 [0 or 1, 2])"""
+        t = self._tokens(tokens)
+        slots = np.empty(len(t), np.int64)
+        cow = np.empty((1, 2), np.int32)
+        n_cow = ctypes.c_int(0)
+        self._check("pkv_bm_append", self._L.pkv_bm_append(
+            self._h, int(seq_id), t.ctypes.data, len(t), slots.ctypes.data, cow.ctypes.data,
+            ctypes.byref(n_cow)))
+        return slots, cow[:n_cow.value].copy()
+
+    def fork(self, parent: int, child: int) -> None:
+        self._check("pkv_bm_fork", self._L.pkv_bm_fork(self._h, int(parent), int(child)))
+
+    def free(self, seq_id: int) -> None:
+        self._check("pkv_bm_free", self._L.pkv_bm_free(self._h, int(seq_id)))
+
+    def _swap(self, fn, what, seq_id):
+        n_blocks, length = ctypes.c_int(0), ctypes.c_int(0)
+        self._L.pkv_bm_block_table(self._h, int(seq_id), None, 0, ctypes.byref(n_blocks),
+                                   ctypes.byref(length))
+        cap = max(n_blocks.value, 1)
+        pairs = np.empty((cap, 2), np.int32)
+        n = ctypes.c_int(0)
+        self._check(what, fn(self._h, int(seq_id), pairs.ctypes.data, cap, ctypes.byref(n)))
+        return pairs[:n.value].copy()
+
+    def swap_out(self, seq_id: int) -> np.ndarray:
+        """-> (device block, host block) pairs int32 [n, 2]"""
+        return self._swap(self._L.pkv_bm_swap_out, "pkv_bm_swap_out", seq_id)
+
+    def swap_in(self, seq_id: int) -> np.ndarray:
+        """-> (host block, device block) pairs int32 [n, 2]"""
+        return self._swap(self._L.pkv_bm_swap_in, "pkv_bm_swap_in", seq_id)
+
+    def block_table(self, seq_id: int):
+        """-> (block ids int32 [n_blocks], sequence length)"""
+        n_blocks, length = ctypes.c_int(0), ctypes.c_int(0)
+        rc = self._L.pkv_bm_block_table(self._h, int(seq_id), None, 0, ctypes.byref(n_blocks),
+                                        ctypes.byref(length))
+        if rc != 0 and n_blocks.value == 0:
+            self._check("pkv_bm_block_table", rc)
+        table = np.empty(max(n_blocks.value, 1), np.int32)
+        self._check("pkv_bm_block_table", self._L.pkv_bm_block_table(
+            self._h, int(seq_id), table.ctypes.data, len(table), ctypes.byref(n_blocks),
+            ctypes.byref(length)))
+        return table[:n_blocks.value].copy(), length.value
+
+    def stats(self) -> dict:
+        st = BlockManagerStats()
+        self._check("pkv_bm_get_stats", self._L.pkv_bm_get_stats(self._h, ctypes.byref(st)))
+        return {f: getattr(st, f) for f, _ in BlockManagerStats._fields_}

@@ -1,0 +1,210 @@
+"""The block manager driving the HIP path end to end (C ABI), against the CPU
+oracle on dense, unpaged sequences.
+
+K and V of a token are a fixed function of (token id, position): seeded
+N(0,1) tables per token and per position, summed and cast to bf16.  So the
+attention of a sequence depends only on its tokens, and a request that reuses a
+cached prefix must give what a full recomputation gives (LLM Inference Server
+page, Stage 1 prefix-cache task: the second request sharing a system prompt
+skips prefill on it and produces identical first-token logits).
+
+The steps: a request with a 200-token system prompt; a second request with the
+same system prompt (200 tokens served from the cache, one copy on write); a
+fork of the second (parallel sampling) and decode steps of all three (the fork
+copies on write); a swap out of the first to pinned host pools, a new request
+that reuses the freed blocks, and a swap back in.  Every prefill and decode
+output is checked against the oracle within 2e-2; the pools start as NaN so
+that a read of an unwritten slot shows up.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as O
+from gpu_run import max_err
+from paged_kv_cache_274_amd import ops
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 2e-2
+H_Q, H_KV, D = 8, 2, 128
+SCALE = 1.0 / np.sqrt(D)
+VOCAB, MAX_POS = 512, 1024
+
+_rng = np.random.default_rng(274100)
+EK = _rng.standard_normal((VOCAB, H_KV, D)).astype(np.float32)
+EV = _rng.standard_normal((VOCAB, H_KV, D)).astype(np.float32)
+PK = _rng.standard_normal((MAX_POS, H_KV, D)).astype(np.float32) * 0.5
+PV = _rng.standard_normal((MAX_POS, H_KV, D)).astype(np.float32) * 0.5
+
+
+def kv_rows(tokens, start):
+    t = np.asarray(tokens)
+    p = np.arange(start, start + len(t))
+    k = torch.from_numpy(EK[t] + PK[p]).to(torch.bfloat16)
+    v = torch.from_numpy(EV[t] + PV[p]).to(torch.bfloat16)
+    return k, v
+
+
+def dense_pool(tokens):
+    """A contiguous pool holding the sequence (blocks 0..n-1 in order), float64."""
+    k, v = kv_rows(tokens, 0)
+    n = len(tokens)
+    nb = -(-n // 16)
+    pad = nb * 16 - n
+
+    def blocks(x):
+        x = torch.cat([x, torch.zeros((pad, H_KV, D), dtype=x.dtype)])
+        return x.reshape(nb, 16, H_KV, D).permute(0, 2, 1, 3).to(torch.float64).numpy()
+    return blocks(k), blocks(v), np.arange(nb, dtype=np.int32)[None, :]
+
+
+def oracle_decode(q, tokens):
+    kc, vc, tbl = dense_pool(tokens)
+    return O.decode(q.to(torch.float64).numpy(), kc, vc, tbl,
+                    np.array([len(tokens)], np.int32), SCALE)
+
+
+def oracle_prefill(q, tokens):
+    kc, vc, tbl = dense_pool(tokens)
+    return O.prefill(q.to(torch.float64).numpy(), np.array([0, q.shape[0]], np.int32), kc, vc,
+                     tbl, np.array([len(tokens)], np.int32), SCALE)
+
+
+class Engine:
+    """The manager, the device pools and the kernels, one step at a time."""
+
+    def __init__(self, n_blocks=96, n_host=48, prefix_cache=True):
+        self.bm = ops.BlockManager(n_blocks, n_host, prefix_cache=prefix_cache)
+        nan = float("nan")
+        self.kc = torch.full((n_blocks, H_KV, 16, D), nan, dtype=torch.bfloat16, device=DEV)
+        self.vc = torch.full_like(self.kc, nan)
+        self.hk = torch.zeros((n_host, H_KV, 16, D), dtype=torch.bfloat16).pin_memory()
+        self.hv = torch.zeros_like(self.hk).pin_memory()
+        self.tokens = {}
+
+    def _copies(self, pairs):
+        if len(pairs):
+            ops.copy_blocks([self.kc, self.vc], torch.from_numpy(pairs).to(DEV))
+
+    def _write(self, slots, tokens, start):
+        k, v = kv_rows(tokens, start)
+        ops.kv_append(k.to(DEV), v.to(DEV), torch.from_numpy(slots).to(DEV), self.kc, self.vc)
+
+    def table(self, sids):
+        rows = [self.bm.block_table(s) for s in sids]
+        width = max(len(t) for t, _ in rows)
+        tbl = np.zeros((len(sids), width), np.int32)
+        for i, (t, _) in enumerate(rows):
+            tbl[i, :len(t)] = t
+        lens = np.array([L for _, L in rows], np.int32)
+        return torch.from_numpy(tbl).to(DEV), torch.from_numpy(lens).to(DEV), int(lens.max())
+
+    def prefill(self, sid, tokens, q_rng):
+        """Admit a prompt; prefill the tokens that are not cached.  Returns
+        (n_cached, GPU output rows, oracle rows)."""
+        n_cached, slots, cow = self.bm.add_sequence(sid, tokens)
+        self._copies(cow)
+        self._write(slots, tokens, 0)
+        self.tokens[sid] = list(tokens)
+        n_new = len(tokens) - n_cached
+        q = torch.from_numpy(q_rng.standard_normal((n_new, H_Q, D)).astype(np.float32)).to(
+            torch.bfloat16)
+        tbl, lens, _ = self.table([sid])
+        out = ops.paged_prefill_attention(q.to(DEV), torch.tensor([0, n_new], dtype=torch.int32,
+                                                                   device=DEV),
+                                          self.kc, self.vc, tbl, lens, n_new, scale=SCALE)
+        torch.cuda.synchronize()
+        return n_cached, out.cpu(), oracle_prefill(q, tokens)
+
+    def decode_step(self, sids, new_tokens, q_rng):
+        """Append one token to each sequence and decode them as one batch."""
+        slots_all, toks = [], []
+        for sid, t in zip(sids, new_tokens):
+            slots, cow = self.bm.append(sid, [t])
+            self._copies(cow)
+            slots_all.append(slots)
+            toks.append((sid, t))
+        for (sid, t), slots in zip(toks, slots_all):
+            self._write(slots, [t], len(self.tokens[sid]))
+            self.tokens[sid].append(t)
+        q = torch.from_numpy(q_rng.standard_normal((len(sids), H_Q, D)).astype(np.float32)).to(
+            torch.bfloat16)
+        tbl, lens, maxc = self.table(sids)
+        out = ops.paged_decode_attention(q.to(DEV), self.kc, self.vc, tbl, lens, maxc,
+                                         scale=SCALE)
+        torch.cuda.synchronize()
+        errs = [max_err(out[i:i + 1].cpu(), oracle_decode(q[i:i + 1], self.tokens[s]))
+                for i, s in enumerate(sids)]
+        return max(errs)
+
+    def swap_out(self, sid):
+        pairs = self.bm.swap_out(sid)
+        ops.swap_blocks([self.kc, self.vc], [self.hk, self.hv], torch.from_numpy(pairs).to(DEV))
+
+    def swap_in(self, sid):
+        pairs = self.bm.swap_in(sid)
+        ops.swap_blocks([self.hk, self.hv], [self.kc, self.vc], torch.from_numpy(pairs).to(DEV))
+
+
+def test_prefix_cache_fork_and_swap_end_to_end():
+    rng = np.random.default_rng(274101)
+    q_rng = np.random.default_rng(274102)
+    system = list(rng.integers(0, VOCAB, 200))
+    e = Engine()
+
+    n0, out0, ref0 = e.prefill("a", system + list(rng.integers(0, VOCAB, 37)), q_rng)
+    assert n0 == 0
+    err = max_err(out0, ref0)
+    n1, out1, ref1 = e.prefill("b", system + list(rng.integers(0, VOCAB, 50)), q_rng)
+    assert n1 == 200 and out1.shape[0] == 50
+    err = max(err, max_err(out1, ref1))
+    st = e.bm.stats()
+    assert st["hit_tokens"] == 200 and st["hit_requests"] == 1
+
+    e.bm.fork("b", "c")
+    e.tokens["c"] = list(e.tokens["b"])
+    for step in range(20):
+        err = max(err, e.decode_step(["a", "b", "c"], list(rng.integers(0, VOCAB, 3)), q_rng))
+
+    e.swap_out("a")
+    n3, out3, ref3 = e.prefill("d", list(rng.integers(0, VOCAB, 300)), q_rng)
+    err = max(err, max_err(out3, ref3))
+    for step in range(5):
+        err = max(err, e.decode_step(["b", "c", "d"], list(rng.integers(0, VOCAB, 3)), q_rng))
+    e.swap_in("a")
+    for step in range(5):
+        err = max(err, e.decode_step(["a", "b", "c", "d"], list(rng.integers(0, VOCAB, 4)),
+                                     q_rng))
+    print(f"manager end-to-end max|err| = {err:.3e}")
+    assert err <= TOL
+
+
+def test_cached_prefix_equals_full_recompute():
+    """The second request's outputs with its system prompt served from the cache
+    equal those of a pool without prefix caching, which prefills all of it."""
+    rng = np.random.default_rng(274103)
+    system = list(rng.integers(0, VOCAB, 200))
+    first = system + list(rng.integers(0, VOCAB, 20))
+    second = system + list(rng.integers(0, VOCAB, 30))
+    cached, plain = Engine(), Engine(prefix_cache=False)
+    cached.prefill(1, first, np.random.default_rng(1))
+    plain.prefill(1, first, np.random.default_rng(1))
+    q_rng_a, q_rng_b = np.random.default_rng(2), np.random.default_rng(3)
+    n, out_c, _ = cached.prefill(2, second, q_rng_a)
+    assert n == 200
+    # the same queries for the last 30 tokens, as the tail of a full prefill
+    q_tail = torch.from_numpy(np.random.default_rng(2).standard_normal((30, H_Q, D))
+                              .astype(np.float32)).to(torch.bfloat16)
+    n2, slots, cow = plain.bm.add_sequence(2, second)
+    assert n2 == 0 and len(cow) == 0
+    plain._write(slots, second, 0)
+    q_full = torch.cat([torch.zeros((230 - 30, H_Q, D), dtype=torch.bfloat16), q_tail])
+    tbl, lens, _ = plain.table([2])
+    out_p = ops.paged_prefill_attention(q_full.to(DEV), torch.tensor([0, 230], dtype=torch.int32,
+                                                                      device=DEV),
+                                        plain.kc, plain.vc, tbl, lens, 230, scale=SCALE)
+    torch.cuda.synchronize()
+    diff = float((out_c.float() - out_p[200:].cpu().float()).abs().max())
+    print(f"cached vs recomputed prefix: max|diff| = {diff:.3e}")
+    assert diff <= TOL

@@ -677,6 +677,10 @@ struct RangeStream {
     QRegs<GC, VPL> q, qn;
     load_q(a, cur, cc, sub, q);
     int t = cur.j0;
+    // Blocks walked so far, and the count after which a raised issue priority
+    // (see decode_split_kernel) drops back to the default.
+    int walked = 0;
+    const int64_t prio_until = (e - (cur.seg0 + cur.j0)) * 3 / 4;
     // Table entries are requested two blocks (and, for the next piece, one
     // piece) ahead of their use: the entry of block t + 1 is in ent[0] at even
     // steps of the inner loop and in ent[1] at odd steps, so each scalar load
@@ -717,6 +721,7 @@ struct RangeStream {
       E = table_entry(cc, min(t + 3, cur.j1 - 1));
       attend_block<T, D, GC, false>(X, q, m, l, acc, a.scale_log2, slot_id, kBlock);
       ++t;
+      if (++walked == prio_until) __builtin_amdgcn_s_setprio(0);
     };
     // Block t (in X) is the piece's last: load the next piece's first block
     // into Y, if there is a next piece, then attend block t, masking the tokens
@@ -793,6 +798,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int W = blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (W >= a.num_splits) return;
   const int HC = a.h_kv * a.n_chunks;
+  // Two workgroups share each CU, and the one dispatched second is younger on
+  // every SIMD it shares; issue arbitration favours the older wave, so the
+  // first round would finish early and leave its CU half occupied for the
+  // tail.  The second half of the grid therefore runs at a raised priority for
+  // the first three quarters of its range (measured on the Llama-3-8B-shaped
+  // batch: 111.4 -> 109.2 us per call; priority over the whole range, or up
+  // to half of it, gained less).
+  if (blockIdx.x >= gridDim.x / 2) __builtin_amdgcn_s_setprio(2);
 
   // Sequences of length 0 get an all-zero output (sequence b by wave b mod splits).
   for (int b0 = W; b0 < a.B; b0 += a.num_splits) {

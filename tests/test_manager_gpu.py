@@ -153,28 +153,28 @@ def test_prefix_cache_fork_and_swap_end_to_end():
     system = list(rng.integers(0, VOCAB, 200))
     e = Engine()
 
-    n0, out0, ref0 = e.prefill("a", system + list(rng.integers(0, VOCAB, 37)), q_rng)
+    n0, out0, ref0 = e.prefill(1, system + list(rng.integers(0, VOCAB, 37)), q_rng)
     assert n0 == 0
     err = max_err(out0, ref0)
-    n1, out1, ref1 = e.prefill("b", system + list(rng.integers(0, VOCAB, 50)), q_rng)
+    n1, out1, ref1 = e.prefill(2, system + list(rng.integers(0, VOCAB, 50)), q_rng)
     assert n1 == 200 and out1.shape[0] == 50
     err = max(err, max_err(out1, ref1))
     st = e.bm.stats()
     assert st["hit_tokens"] == 200 and st["hit_requests"] == 1
 
-    e.bm.fork("b", "c")
-    e.tokens["c"] = list(e.tokens["b"])
+    e.bm.fork(2, 3)
+    e.tokens[3] = list(e.tokens[2])
     for step in range(20):
-        err = max(err, e.decode_step(["a", "b", "c"], list(rng.integers(0, VOCAB, 3)), q_rng))
+        err = max(err, e.decode_step([1, 2, 3], list(rng.integers(0, VOCAB, 3)), q_rng))
 
-    e.swap_out("a")
-    n3, out3, ref3 = e.prefill("d", list(rng.integers(0, VOCAB, 300)), q_rng)
+    e.swap_out(1)
+    n3, out3, ref3 = e.prefill(4, list(rng.integers(0, VOCAB, 300)), q_rng)
     err = max(err, max_err(out3, ref3))
     for step in range(5):
-        err = max(err, e.decode_step(["b", "c", "d"], list(rng.integers(0, VOCAB, 3)), q_rng))
-    e.swap_in("a")
+        err = max(err, e.decode_step([2, 3, 4], list(rng.integers(0, VOCAB, 3)), q_rng))
+    e.swap_in(1)
     for step in range(5):
-        err = max(err, e.decode_step(["a", "b", "c", "d"], list(rng.integers(0, VOCAB, 4)),
+        err = max(err, e.decode_step([1, 2, 3, 4], list(rng.integers(0, VOCAB, 4)),
                                      q_rng))
     print(f"manager end-to-end max|err| = {err:.3e}")
     assert err <= TOL

@@ -527,6 +527,23 @@ def summarize_stats(stats_csv, bench_json, extra):
     for r in rows:
         text.append(f"#   {int(r['Calls']):6d} {float(r['AverageNs']):12.1f} {int(r['MinNs']):10d} "
                     f"{int(r['MaxNs']):10d}  {r['Name'][:110]}")
+    trace = os.path.join(os.path.dirname(stats_csv),
+                         os.path.basename(stats_csv).replace("kernel_stats", "kernel_trace"))
+    if os.path.exists(trace):
+        # copy_blocks runs for several legs; its dispatches are told apart by grid
+        grids = defaultdict(list)
+        with open(trace) as f:
+            for r in csv.DictReader(f):
+                if "copy_blocks_kernel" in r["Kernel_Name"]:
+                    us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                    grids[int(r["Grid_Size_X"]) // 256].append(us)
+        legs = {64: "copy on write, 64 blocks x 2 pools (4 MiB read + 4 MiB written)",
+                1024: "copy on write, 1024 blocks x 2 pools (64 MiB read + 64 MiB written)",
+                512: "swap out and in, 512 blocks x 2 pools (32 MiB over PCIe)"}
+        text.append("# copy_blocks_kernel by leg (kernel trace of the same run): calls, median us, min us")
+        for n, v in sorted(grids.items()):
+            text.append(f"#   {len(v):4d} {statistics.median(v):10.2f} {min(v):10.2f}  "
+                        f"{legs.get(n, f'{n} pairs')}")
     text += [
         f"# decode call = split pass + combine pass averages: {call_ns / 1e3:.2f} us (rocprofv3);",
         f"# HIP events in the same run: {line['roofline']['avg_us']} us per call over back-to-back "

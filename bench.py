@@ -335,6 +335,32 @@ def time_blocks(dev: str, iters: int = 20):
     return res
 
 
+def time_manager(steps: int = 200):
+    """Host cost of the block manager for the decode batch's shape, through the
+    binding: 64 prompts of 2048 tokens sharing a 208-token prefix admitted,
+    then `steps` decode steps of one token each (append_batch + block_tables,
+    which give the step's slot_mapping, copies and tables)."""
+    rng = np.random.default_rng(274011)
+    bm = ops.BlockManager(64 * (2048 + steps) // 16 + 256)
+    prefix = list(rng.integers(0, 32000, 208))
+    t0 = time.perf_counter()
+    for i in range(64):
+        bm.add_sequence(i, prefix + list(rng.integers(0, 32000, 2048 - 208)))
+    add_s = time.perf_counter() - t0
+    ids = np.arange(64, dtype=np.int64)
+    toks = rng.integers(0, 32000, (steps, 64)).astype(np.int32)
+    t0 = time.perf_counter()
+    for k in range(steps):
+        bm.append_batch(ids, toks[k])
+        bm.block_tables(ids, max_blocks=(2048 + steps) // 16 + 1)
+    step_s = (time.perf_counter() - t0) / steps
+    st = bm.stats()
+    return {"prompts": 64, "prompt_tokens": 2048, "shared_prefix_tokens": 208,
+            "add_sequence_avg_us": round(add_s / 64 * 1e6, 1),
+            "prefix_hit_tokens": st["hit_tokens"],
+            "decode_step_64_seqs_us": round(step_s * 1e6, 1)}
+
+
 def cpu_baseline(w: W.Workload, reps: int):
     """The oracle (append + decode of the whole step) on the host cores."""
     import oracle.attention as O
@@ -676,6 +702,7 @@ def main(argv=None):
 
     copy_gbs = time_copy(dev)
     blocks = time_blocks(dev)
+    blocks["manager"] = time_manager()
     traffic = measured_traffic(args.config)
     mfma = measured_mfma()
 

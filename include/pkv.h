@@ -339,6 +339,22 @@ int pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id, const int32_t* to
 int pkv_bm_append(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens, int n_tokens,
                   int64_t* slots, int32_t* cow_pairs, int* n_cow);
 
+/* One decode step of a batch: token tokens[i] is appended to sequence
+ * seq_ids[i] (distinct, resident) for i < n, in that order, as by n calls of
+ * pkv_bm_append; slots[n] receives their slots (the step's slot_mapping) and
+ * cow_pairs (room for n pairs) the copies on write to run first.  All or
+ * nothing: PKV_ERR_NO_BLOCKS if the free queue cannot supply the whole step. */
+int pkv_bm_append_batch(pkv_block_manager* bm, int n, const int64_t* seq_ids,
+                        const int32_t* tokens, int64_t* slots, int32_t* cow_pairs, int* n_cow);
+
+/* Block tables and context lengths of n resident sequences, laid out as the
+ * attention calls take them: tables [n, max_blocks] (host int32, row i holds
+ * sequence seq_ids[i]'s blocks, then zeros) and context_lens [n].
+ * PKV_ERR_INVALID_ARG if a sequence is unknown, swapped out or has more than
+ * max_blocks blocks (nothing written). */
+int pkv_bm_block_tables(const pkv_block_manager* bm, int n, const int64_t* seq_ids,
+                        int32_t* tables, int max_blocks, int32_t* context_lens);
+
 /* child shares every block of parent (parallel sampling); later writes copy on
  * write. */
 int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);

@@ -183,6 +183,24 @@ class BlockManager:
         self._write(seq, list(tokens), slots, pairs)
         return slots, pairs
 
+    def append_batch(self, sids, tokens):
+        """One token per sequence, in order, all or nothing.  Returns (slots,
+        cow_pairs)."""
+        if len(set(sids)) != len(sids):
+            raise KeyError("a sequence named twice")
+        import copy
+        saved = copy.deepcopy(self.__dict__)
+        slots, pairs = [], []
+        try:
+            for sid, t in zip(sids, tokens):
+                s, p = self.append(sid, [t])
+                slots += s
+                pairs += p
+        except NoBlocks:
+            self.__dict__.update(saved)
+            raise
+        return slots, pairs
+
     def fork(self, parent, child):
         p = self.seqs[parent]
         if child in self.seqs or p["swapped"]:

@@ -316,6 +316,63 @@ int pkv_bm_append(pkv_block_manager* m, int64_t seq_id, const int32_t* tokens, i
   return PKV_OK;
 }
 
+int pkv_bm_append_batch(pkv_block_manager* m, int n, const int64_t* seq_ids,
+                        const int32_t* tokens, int64_t* slots, int32_t* cow_pairs, int* n_cow) {
+  if (!m || n < 0 || !n_cow || (n > 0 && (!seq_ids || !tokens || !slots || !cow_pairs)))
+    return PKV_ERR_INVALID_ARG;
+  std::vector<Seq*> ss((size_t)n);
+  std::unordered_map<int64_t, int> seen;
+  // Blocks the whole step takes from the free queue, in order: a sequence at a
+  // block boundary takes a new block; one writing into a block that others
+  // still hold takes a copy, after which that block has one holder fewer.
+  std::unordered_map<int32_t, int32_t> copied;  // block -> holders gone to copies
+  int64_t need = 0;
+  for (int i = 0; i < n; ++i) {
+    auto it = m->seqs.find(seq_ids[i]);
+    if (it == m->seqs.end() || it->second.swapped || seen.count(seq_ids[i]))
+      return PKV_ERR_INVALID_ARG;
+    seen[seq_ids[i]] = i;
+    Seq& s = it->second;
+    ss[(size_t)i] = &s;
+    const int64_t L = (int64_t)s.tokens.size();
+    if (L % kB == 0) {
+      ++need;
+    } else {
+      const int32_t b = s.table[L / kB];
+      if (m->blocks[b].ref - copied[b] > 1) {
+        ++need;
+        ++copied[b];
+      }
+    }
+  }
+  if (need > m->n_free) return PKV_ERR_NO_BLOCKS;
+  *n_cow = 0;
+  for (int i = 0; i < n; ++i) m->write(*ss[(size_t)i], tokens + i, 1, slots + i, cow_pairs, n_cow);
+  return PKV_OK;
+}
+
+int pkv_bm_block_tables(const pkv_block_manager* m, int n, const int64_t* seq_ids,
+                        int32_t* tables, int max_blocks, int32_t* context_lens) {
+  if (!m || n < 0 || max_blocks < 0 ||
+      (n > 0 && (!seq_ids || !context_lens || (max_blocks > 0 && !tables))))
+    return PKV_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i) {
+    auto it = m->seqs.find(seq_ids[i]);
+    if (it == m->seqs.end() || it->second.swapped ||
+        (int64_t)it->second.table.size() > max_blocks)
+      return PKV_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < n; ++i) {
+    const Seq& s = m->seqs.find(seq_ids[i])->second;
+    int32_t* row = tables + (size_t)i * max_blocks;
+    const size_t nb = s.table.size();
+    if (nb) memcpy(row, s.table.data(), sizeof(int32_t) * nb);
+    for (size_t j = nb; j < (size_t)max_blocks; ++j) row[j] = 0;
+    context_lens[i] = (int32_t)s.tokens.size();
+  }
+  return PKV_OK;
+}
+
 int pkv_bm_fork(pkv_block_manager* m, int64_t parent, int64_t child) {
   if (!m) return PKV_ERR_INVALID_ARG;
   auto it = m->seqs.find(parent);

@@ -27,7 +27,8 @@ EXPORTED = ("kv_append", "paged_decode_attention", "paged_prefill_attention",
             "copy_blocks", "swap_blocks",
             "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_sequence", "pkv_bm_append",
             "pkv_bm_fork", "pkv_bm_free", "pkv_bm_swap_out", "pkv_bm_swap_in",
-            "pkv_bm_block_table", "pkv_bm_get_stats", "pkv_kv_cache_bytes")
+            "pkv_bm_block_table", "pkv_bm_get_stats", "pkv_kv_cache_bytes",
+            "pkv_bm_append_batch", "pkv_bm_block_tables")
 PKV_ERR_NO_BLOCKS = 5
 
 _lib = None
@@ -102,8 +103,11 @@ def lib() -> ctypes.CDLL:
     L.pkv_bm_swap_in.argtypes = [vp, i64, vp, i32, ip]
     L.pkv_bm_block_table.argtypes = [vp, i64, vp, i32, ip, ip]
     L.pkv_bm_get_stats.argtypes = [vp, ctypes.POINTER(BlockManagerStats)]
+    L.pkv_bm_append_batch.argtypes = [vp, i32, vp, vp, vp, vp, ip]
+    L.pkv_bm_block_tables.argtypes = [vp, i32, vp, vp, i32, vp]
     for f in ("pkv_bm_add_sequence", "pkv_bm_append", "pkv_bm_fork", "pkv_bm_free",
-              "pkv_bm_swap_out", "pkv_bm_swap_in", "pkv_bm_block_table", "pkv_bm_get_stats"):
+              "pkv_bm_swap_out", "pkv_bm_swap_in", "pkv_bm_block_table", "pkv_bm_get_stats",
+              "pkv_bm_append_batch", "pkv_bm_block_tables"):
         getattr(L, f).restype = i32
     L.pkv_kv_cache_bytes.argtypes = [i32, i32, i32, i64, i64, i32, i32]
     L.pkv_kv_cache_bytes.restype = i64
@@ -463,6 +467,33 @@ class BlockManager:
             self._h, int(seq_id), t.ctypes.data, len(t), slots.ctypes.data, cow.ctypes.data,
             ctypes.byref(n_cow)))
         return slots, cow[:n_cow.value].copy()
+
+    def append_batch(self, seq_ids, tokens):
+        """One token per sequence (a decode step) -> (slots int64 [n],
+        cow_pairs int32 [k, 2])"""
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64).reshape(-1))
+        t = self._tokens(tokens)
+        _need(len(ids) == len(t), "one token per sequence")
+        slots = np.empty(len(t), np.int64)
+        cow = np.empty((max(len(t), 1), 2), np.int32)
+        n_cow = ctypes.c_int(0)
+        self._check("pkv_bm_append_batch", self._L.pkv_bm_append_batch(
+            self._h, len(t), ids.ctypes.data, t.ctypes.data, slots.ctypes.data, cow.ctypes.data,
+            ctypes.byref(n_cow)))
+        return slots, cow[:n_cow.value].copy()
+
+    def block_tables(self, seq_ids, max_blocks: Optional[int] = None):
+        """-> (tables int32 [n, max_blocks], context_lens int32 [n]) for the
+        attention calls; max_blocks defaults to the longest table."""
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64).reshape(-1))
+        if max_blocks is None:
+            max_blocks = max([len(self.block_table(int(i))[0]) for i in ids] + [1])
+        tables = np.empty((len(ids), max_blocks), np.int32)
+        lens = np.empty(len(ids), np.int32)
+        self._check("pkv_bm_block_tables", self._L.pkv_bm_block_tables(
+            self._h, len(ids), ids.ctypes.data, tables.ctypes.data, max_blocks,
+            lens.ctypes.data))
+        return tables, lens
 
     def fork(self, parent: int, child: int) -> None:
         self._check("pkv_bm_fork", self._L.pkv_bm_fork(self._h, int(parent), int(child)))

@@ -195,9 +195,12 @@ def _trace(seed, n_ops, n_blocks, n_host, prefix_cache=True):
             cut = int(rng.integers(0, len(sp) + 1))
             tail = list(rng.integers(0, 6, int(rng.integers(0, 40))))
             ops_.append(("add", i, sp[:cut] + tail))
-        elif r < 0.6:
+        elif r < 0.52:
             ops_.append(("append", int(rng.integers(0, 1 << 30)),
                          list(rng.integers(0, 6, int(rng.integers(1, 6))))))
+        elif r < 0.6:
+            ops_.append(("batch", int(rng.integers(0, 1 << 30)),
+                         list(rng.integers(0, 6, int(rng.integers(1, 9))))))
         elif r < 0.7:
             ops_.append(("fork", int(rng.integers(0, 1 << 30)), 100000 + i))
         elif r < 0.82:
@@ -217,6 +220,32 @@ def _run(m, lib_m, trace, n_blocks, n_host, check_every=1):
     ran = 0
     for k, (op, a, b) in enumerate(trace):
         if op != "add" and not live:
+            continue
+        if op == "batch":
+            resident = [x for x in live if not m.seqs[x]["swapped"]]
+            if not resident:
+                continue
+            k0 = a % len(resident)
+            sids = (resident[k0:] + resident[:k0])[:len(b)]
+            toks = b[:len(sids)]
+            starts = [len(m.seqs[x]["tokens"]) for x in sids]
+            try:
+                ro = m.append_batch(sids, toks)
+            except OBM.NoBlocks:
+                ro = "no-blocks"
+            if lib_m is not None:
+                try:
+                    rl = lib_m.append_batch(sids, toks)
+                except ops.NoBlocksError:
+                    rl = "no-blocks"
+                assert isinstance(rl, str) == isinstance(ro, str), k
+                if not isinstance(ro, str):
+                    assert list(rl[0]) == ro[0] and [tuple(p) for p in rl[1]] == ro[1], k
+            if not isinstance(ro, str):
+                cm.copy(ro[1], cm.dev, cm.dev)
+                for sl, t, st in zip(ro[0], toks, starts):
+                    cm.write([sl], [t], st)
+            ran += 1
             continue
         sid = live[a % len(live)] if op != "add" else a
         sw = op != "add" and m.seqs[sid]["swapped"]
@@ -299,6 +328,13 @@ def _run(m, lib_m, trace, n_blocks, n_host, check_every=1):
                         t, L = lib_m.block_table(s_id)
                         assert list(t) == s["table"] and L == len(s["tokens"]), k
             if lib_m:
+                res = [x for x, sq in m.seqs.items() if not sq["swapped"]]
+                if res:
+                    tb, ln = lib_m.block_tables(res)
+                    for i, x in enumerate(res):
+                        nb = len(m.seqs[x]["table"])
+                        assert list(tb[i, :nb]) == m.seqs[x]["table"], k
+                        assert not tb[i, nb:].any() and ln[i] == len(m.seqs[x]["tokens"]), k
                 so, sl = m.stats(), lib_m.stats()
                 assert (sl["free_blocks"], sl["host_free_blocks"], sl["cached_blocks"],
                         sl["cached_free_blocks"], sl["hit_tokens"], sl["query_tokens"],
@@ -325,6 +361,37 @@ def test_library_matches_oracle_on_random_traces(seed, n_blocks, n_host, prefix)
     assert ran > 350
     st = m.stats()
     assert st["hit_tokens"] > 0 or not prefix
+
+
+def test_batch_append_copies_for_forked_siblings_once():
+    """Three forks of one sequence whose last block holds 4 tokens append in one
+    step: the first two copy the shared block, the last one then holds it alone
+    and writes in place."""
+    m = OBM.BlockManager(8)
+    lib_m = ops.BlockManager(8)
+    for mm in (m, lib_m):
+        mm.add_sequence(0, list(range(20)))        # blocks 0, 1
+        mm.fork(0, 1)
+        mm.fork(0, 2)
+    slots, pairs = m.append_batch([0, 1, 2], [7, 8, 9])
+    assert pairs == [(1, 2), (1, 3)] and slots == [2 * 16 + 4, 3 * 16 + 4, 1 * 16 + 4]
+    ls, lp = lib_m.append_batch([0, 1, 2], [7, 8, 9])
+    assert list(ls) == slots and [tuple(p) for p in lp] == pairs
+    with pytest.raises(KeyError):
+        m.append_batch([0, 0], [1, 2])
+    with pytest.raises(ops.PkvError):
+        lib_m.append_batch([0, 0], [1, 2])
+    # not enough blocks for the step: nothing changes
+    small, small_l = OBM.BlockManager(3), ops.BlockManager(3)
+    for mm in (small, small_l):
+        mm.add_sequence(0, list(range(16)))
+        mm.add_sequence(1, list(range(50, 66)))
+    before = small.stats()
+    with pytest.raises(OBM.NoBlocks):
+        small.append_batch([0, 1], [1, 2])          # two new blocks, one free
+    with pytest.raises(ops.NoBlocksError):
+        small_l.append_batch([0, 1], [1, 2])
+    assert small.stats() == before and small_l.stats()["free_blocks"] == 1
 
 
 def test_library_errors():

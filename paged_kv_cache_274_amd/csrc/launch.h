@@ -112,6 +112,7 @@ struct PrefillArgs {
   const int32_t* context_lens;
   int S, T_q, max_q_len, h_q, h_kv, g, n_blocks, max_blocks_per_seq;
   float scale_log2;
+  int longest_first;  // set by the launcher: sequence planes taken longest context first
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d_h, hipStream_t stream);

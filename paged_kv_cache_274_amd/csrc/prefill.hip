@@ -105,6 +105,47 @@ __device__ __forceinline__ void tile_barrier() {
 // group G takes tiles G, G + KS, G + 2 KS, ... with three buffers of its own,
 // and the groups' softmax states are merged at the end.  KS = 2 halves the
 // serial key walk of the longest rows when the grid alone cannot fill the chip.
+// The sequence of grid plane z when the planes are taken longest context first
+// (ties: lower index), for grids larger than the chip holds at once: the
+// longest key walks then start in the first round instead of whenever their
+// plane comes up (longest-processing-time order).  Each lane holds the lengths
+// of sequences lane, lane + 64, ... (a.S <= kLptMaxSeqs) and ranks its own
+// against all of them; every wave computes the same answer.
+constexpr int kLptMaxSeqs = 256;
+__device__ __forceinline__ int longest_first_sequence(const PrefillArgs& a, int z) {
+  constexpr int kC = kLptMaxSeqs / 64;
+  const int lane = threadIdx.x & 63;
+  const int cap = a.max_blocks_per_seq * kBlock;
+  int len[kC];
+#pragma unroll
+  for (int c = 0; c < kC; ++c) {
+    const int j = c * 64 + lane;
+    len[c] = j < a.S ? max(0, min(a.context_lens[j], cap)) : -1;
+  }
+  int found = z;
+#pragma unroll
+  for (int c = 0; c < kC; ++c) {
+    if (c * 64 >= a.S) break;
+    const int j = c * 64 + lane;
+    int rank = 0;
+#pragma unroll
+    for (int ci = 0; ci < kC; ++ci) {
+      if (ci * 64 >= a.S) break;
+      const int n = min(64, a.S - ci * 64);
+      for (int t = 0; t < n; ++t) {
+        const int li = __builtin_amdgcn_readlane(len[ci], t);
+        rank += (li > len[c]) || (li == len[c] && ci * 64 + t < j);
+      }
+    }
+    const uint64_t hit = __ballot(j < a.S && rank == z);
+    if (hit) {
+      found = c * 64 + __builtin_ctzll(hit);
+      break;
+    }
+  }
+  return __builtin_amdgcn_readfirstlane(found);
+}
+
 template <int D, int KS>
 __global__ __launch_bounds__(256 * KS) void prefill_bf16_kernel(PrefillArgs a) {
   using Tl = PfTile<D>;
@@ -115,7 +156,7 @@ __global__ __launch_bounds__(256 * KS) void prefill_bf16_kernel(PrefillArgs a) {
 
   // Workgroups with the most key tiles (the last rows of a sequence) first.
   const int bx = gridDim.x - 1 - blockIdx.x;
-  const int s = blockIdx.z;
+  const int s = a.longest_first ? longest_first_sequence(a, blockIdx.z) : (int)blockIdx.z;
   const int kvh = blockIdx.y;
   const int g = a.g;
   const int q0 = a.cu_seqlens_q[s];
@@ -417,16 +458,22 @@ static hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.max_q_len * a.g;
   const int64_t gx = (rows + kPfRows - 1) / kPfRows;
   const dim3 grid((unsigned)gx, a.h_kv, a.S);
+  // Order the sequence planes longest first when the grid takes more than one
+  // round of the chip (one workgroup per compute unit is assumed: the tile
+  // buffers of d_h = 128 fill most of its LDS) and the ranking stays cheap.
+  PrefillArgs args = a;
+  const int cus = compute_units();
+  args.longest_first = a.S > 1 && a.S <= kLptMaxSeqs && cus > 0 && gx * a.h_kv * a.S > cus;
   // Split the key walk over two wave groups when the grid has no more
   // workgroups than the chip has compute units (d_h = 64: eight waves of this
   // kernel fit one compute unit's registers).
   if constexpr (D == 64) {
     if (gx * a.h_kv * a.S <= compute_units()) {
-      hipLaunchKernelGGL((prefill_bf16_kernel<D, 2>), grid, dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, 2>), grid, dim3(512), 0, stream, args);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, 1>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, 1>), grid, dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 

@@ -265,6 +265,24 @@ def test_multi_token_decode_verify(n_s):
     assert max_err(res.prefill[last], one.double().numpy()) <= 2e-2
 
 
+@pytest.mark.parametrize("S,n_s,lens_of", [
+    (40, 3, lambda rng, S: rng.integers(4, 1500, size=S)),
+    (200, 2, lambda rng, S: rng.integers(1, 40, size=S) * 7),     # many equal lengths
+    (300, 2, lambda rng, S: rng.integers(3, 200, size=S))])
+def test_prefill_grid_beyond_one_round(S, n_s, lens_of):
+    """Grids with more workgroups than the chip holds at once take their
+    sequence planes longest context first (ties by index; S <= 256), so the
+    sequence a workgroup serves is not its plane index; with S > 256 the
+    index order stays.  Every row matches the oracle either way."""
+    rng = np.random.default_rng(500 + S)
+    lens = [max(int(x), n_s) for x in lens_of(rng, S)]
+    w = W.build("many", rng, dtype="bf16", h_q=16, h_kv=8, d=128,
+                prefill=[(L, n_s) for L in lens], free_frac=0.05, poison=True)
+    res = run(w, DEV)
+    kc_ref, vc_ref = check_append(w, res)
+    check_prefill(w, res, kc_ref, vc_ref)
+
+
 @pytest.mark.parametrize("scale", [-0.2, 1.0])
 def test_negative_and_large_scale(scale):
     """Any finite scale: a negative one reverses the ranking of the keys, a

@@ -208,3 +208,69 @@ def test_cached_prefix_equals_full_recompute():
     diff = float((out_c.float() - out_p[200:].cpu().float()).abs().max())
     print(f"cached vs recomputed prefix: max|diff| = {diff:.3e}")
     assert diff <= TOL
+
+
+def test_int8_cache_under_the_manager():
+    """The INT8 cache (codes and one float32 scale per token head row, four pools
+    under one block mapping) driven by the manager: a shared prompt, a fork, and
+    decode steps whose copies on write move codes and scales together.  The
+    pools must equal the oracle's bit for bit after every step and the INT8
+    decode must be within 2e-2 of the oracle's attention over the dequantised
+    cache."""
+    import oracle.blocks as OB
+    import oracle.quant as Q
+    rng = np.random.default_rng(274104)
+    q_rng = np.random.default_rng(274105)
+    n_blocks = 40
+    bm = ops.BlockManager(n_blocks)
+    dev_pools = [torch.zeros((n_blocks, H_KV, 16, D), dtype=torch.int8, device=DEV),
+                 torch.zeros((n_blocks, H_KV, 16, D), dtype=torch.int8, device=DEV),
+                 torch.full((n_blocks, H_KV, 16), float("nan"), device=DEV),
+                 torch.full((n_blocks, H_KV, 16), float("nan"), device=DEV)]
+    ref = [p.cpu().numpy() for p in dev_pools]
+    tokens = {}
+
+    def write(slots, toks, start):
+        k, v = kv_rows(toks, start)
+        ops.kv_append_int8(k.to(DEV), v.to(DEV), torch.from_numpy(slots).to(DEV), *dev_pools)
+        return list(Q.kv_append_int8(k.float().numpy(), v.float().numpy(), slots, *ref))
+
+    def copies(pairs):
+        nonlocal ref
+        if len(pairs):
+            ops.copy_blocks(dev_pools, torch.from_numpy(pairs).to(DEV))
+            ref = OB.copy_blocks(ref, ref, pairs)
+
+    system = list(rng.integers(0, VOCAB, 100))
+    for sid, extra in ((1, 30), (2, 45)):
+        toks = system + list(rng.integers(0, VOCAB, extra))
+        n_cached, slots, cow = bm.add_sequence(sid, toks)
+        copies(cow)
+        ref = write(slots, toks, 0)
+        tokens[sid] = toks
+    assert n_cached == 100
+    bm.fork(2, 3)
+    tokens[3] = list(tokens[2])
+    err = 0.0
+    for step in range(6):
+        sids = [1, 2, 3]
+        new = list(rng.integers(0, VOCAB, 3))
+        slots, cow = bm.append_batch(sids, new)
+        copies(cow)
+        for sid, t, sl in zip(sids, new, slots):
+            ref = write(np.array([sl]), [t], len(tokens[sid]))
+            tokens[sid].append(t)
+        tbl, lens = bm.block_tables(sids)
+        q = torch.from_numpy(q_rng.standard_normal((3, H_Q, D)).astype(np.float32)).to(
+            torch.bfloat16)
+        out = ops.paged_decode_attention_int8(q.to(DEV), *dev_pools, torch.from_numpy(tbl).to(DEV),
+                                              torch.from_numpy(lens).to(DEV), int(lens.max()),
+                                              scale=SCALE)
+        torch.cuda.synchronize()
+        for g, r in zip(dev_pools, ref):
+            a = g.cpu().numpy()
+            assert a.tobytes() == np.ascontiguousarray(r).tobytes(), f"pools differ at step {step}"
+        want = Q.decode_int8(q.to(torch.float64).numpy(), *ref, tbl, lens, SCALE)
+        err = max(err, max_err(out.cpu(), want))
+    print(f"int8 cache under the manager: decode max|err| = {err:.3e}")
+    assert err <= TOL

@@ -71,12 +71,13 @@ int debug_check_slots(const int64_t* slot_mapping, int T, int n_blocks, hipStrea
 // pinned host memory through its device mapping.  False for memory the GPU
 // cannot reach (pageable host memory, unknown pointers); the runtime's error is
 // cleared so that it is not reported by a later launch check.
-bool device_address(const void* p, const void** out) {
+bool device_address(const void* p, const void** out, bool* on_host) {
   hipPointerAttribute_t a;
   if (hipPointerGetAttributes(&a, p) != hipSuccess) {
     (void)hipGetLastError();
     return false;
   }
+  *on_host = false;
   if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) {
     *out = p;
     return true;
@@ -92,6 +93,7 @@ bool device_address(const void* p, const void** out) {
       return false;
     }
     *out = d;
+    *on_host = true;
     return true;
   }
   return false;
@@ -134,24 +136,28 @@ int copy_call(const void* const* src, void* const* dst, const int64_t* block_byt
   if (!pairs || ((uintptr_t)pairs & 3u)) return PKV_ERR_INVALID_ARG;
   pkv::CopyPools p;
   memset(&p, 0, sizeof(p));
+  bool device_only = true;
   for (int i = 0; i < n_pools; ++i) {
     const void* s_dev;
     const void* d_dev;
-    if (!device_address(src[i], &s_dev) || !device_address(dst[i], &d_dev))
+    bool s_host, d_host;
+    if (!device_address(src[i], &s_dev, &s_host) || !device_address(dst[i], &d_dev, &d_host))
       return PKV_ERR_INVALID_ARG;
+    device_only = device_only && !s_host && !d_host;
     p.src[i] = (const uint4*)s_dev;
     p.dst[i] = (uint4*)d_dev;
     p.vecs[i] = block_bytes[i] / 16;
   }
   const void* pairs_dev;
-  if (!device_address(pairs, &pairs_dev)) return PKV_ERR_INVALID_ARG;
+  bool pairs_host;
+  if (!device_address(pairs, &pairs_dev, &pairs_host)) return PKV_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   if (debug_checks()) {
     const int rc = debug_check_pairs(pairs, n_pairs, n_src, n_dst, same_set, s);
     if (rc != PKV_OK) return rc;
   }
   return from_hip(pkv::launch_copy_blocks(p, n_pools, (const int32_t*)pairs_dev, n_pairs, n_src,
-                                          n_dst, s));
+                                          n_dst, device_only, s));
 }
 
 // Pool element type of a decode dtype code; false for an unknown code.

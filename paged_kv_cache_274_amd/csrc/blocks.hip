@@ -19,10 +19,35 @@
 
 namespace pkv {
 
+// Every byte is read once and written once.  Between device pools both go with
+// the non-temporal hint: measured on 1024 decode-shaped blocks, it halves the
+// copy time (49 -> 24 us, 5.6 TB/s read + write).  Through pinned host memory
+// the hint costs PCIe rate (swap of 32 MiB: 53 -> 49 GB/s), so swaps use plain
+// accesses.
+template <bool NT>
+__device__ __forceinline__ uint4 copy_load(const uint4* p) {
+  if constexpr (NT) {
+    const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(x.x, x.y, x.z, x.w);
+  } else {
+    return *p;
+  }
+}
+template <bool NT>
+__device__ __forceinline__ void copy_store(uint4* p, const uint4& v) {
+  if constexpr (NT) {
+    const u32x4_t x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(p));
+  } else {
+    *p = v;
+  }
+}
+
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 8;
 constexpr int kCopySliceVecs = kCopyThreads * kCopyUnroll;  // 2048 vectors = 32 KiB
 
+template <bool NT>
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
     CopyPools p, const int32_t* __restrict__ pairs, int n_src_blocks, int n_dst_blocks) {
   const int pool = blockIdx.y;
@@ -39,25 +64,30 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u) {
     const int64_t i = (int64_t)u * kCopyThreads + threadIdx.x;
-    if (i < n) r[u] = s[i];
+    if (i < n) r[u] = copy_load<NT>(s + i);
   }
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u) {
     const int64_t i = (int64_t)u * kCopyThreads + threadIdx.x;
-    if (i < n) d[i] = r[u];
+    if (i < n) copy_store<NT>(d + i, r[u]);
   }
 }
 
 hipError_t launch_copy_blocks(const CopyPools& p, int n_pools, const int32_t* pairs, int n_pairs,
-                              int n_src_blocks, int n_dst_blocks, hipStream_t stream) {
+                              int n_src_blocks, int n_dst_blocks, bool device_only,
+                              hipStream_t stream) {
   int64_t most = 0;
   for (int i = 0; i < n_pools; ++i) most = p.vecs[i] > most ? p.vecs[i] : most;
   const int64_t slices = (most + kCopySliceVecs - 1) / kCopySliceVecs;
   if (n_pairs <= 0 || n_pools <= 0 || slices <= 0) return hipSuccess;
   if (slices > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)n_pairs, (unsigned)n_pools,
-                                              (unsigned)slices),
-                     dim3(kCopyThreads), 0, stream, p, pairs, n_src_blocks, n_dst_blocks);
+  const dim3 grid((unsigned)n_pairs, (unsigned)n_pools, (unsigned)slices);
+  if (device_only)
+    hipLaunchKernelGGL(copy_blocks_kernel<true>, grid, dim3(kCopyThreads), 0, stream, p, pairs,
+                       n_src_blocks, n_dst_blocks);
+  else
+    hipLaunchKernelGGL(copy_blocks_kernel<false>, grid, dim3(kCopyThreads), 0, stream, p, pairs,
+                       n_src_blocks, n_dst_blocks);
   return hipGetLastError();
 }
 

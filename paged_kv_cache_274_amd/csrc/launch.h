@@ -129,9 +129,12 @@ struct CopyPools {
 };
 
 // pairs: int32 [n_pairs][2] (source block, destination block), device-visible.
-// A pair with an index out of range is skipped.  Returns hipErrorInvalidValue
-// when a block is too large for the grid (more than 65535 slices of 32 KiB).
+// A pair with an index out of range is skipped.  device_only: every pool is
+// device memory (the copy then streams with the non-temporal hint).  Returns
+// hipErrorInvalidValue when a block is too large for the grid (more than 65535
+// slices of 32 KiB).
 hipError_t launch_copy_blocks(const CopyPools& p, int n_pools, const int32_t* pairs, int n_pairs,
-                              int n_src_blocks, int n_dst_blocks, hipStream_t stream);
+                              int n_src_blocks, int n_dst_blocks, bool device_only,
+                              hipStream_t stream);
 
 }  // namespace pkv

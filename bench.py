@@ -31,6 +31,8 @@ Printed as one JSON line:
              INT8 cache: bytes = sum_b L_b * 2 * h_kv * (d_h + 4) (codes and
              one float32 scale per token head row), time over back-to-back
              calls, and kv_append_int8 of the step's new tokens
+  mixed_step the whole continuous-batch step of the Qwen2.5-0.5B-shaped
+             workload (append, prefill, decode on one stream), with its parts
   blocks     copy_blocks (copy on write inside a device pool set) and
              swap_blocks (device <-> pinned host pool sets) on decode-shaped
              pools, with a plain torch copy to and from pinned memory beside
@@ -695,6 +697,22 @@ def main(argv=None):
     r5 = Resident(w5, dev)
     r5.append(0)
     pf_b2b_ms, pf_ms = time_prefill(r5)
+
+    # the whole mixed continuous-batch step of the same workload: append of all
+    # new tokens, then the prefill of the 4 prompts, then the decode of the 60
+    # running sequences, on one stream
+    kc5, vc5 = r5.pools[0]
+    app5 = ops.bind_kv_append(r5.k_new, r5.v_new, r5.slots, kc5, vc5)
+    dec5 = ops.bind_decode(r5.q, kc5, vc5, r5.tables, r5.lens, w5.dec_max_context_len,
+                           r5.out, r5.ws, scale=w5.scale)
+
+    def mixed(i):
+        app5()
+        r5.prefill(0)
+        dec5()
+    mixed_ms = time_calls(mixed, args.steps, warmup=5)
+    mixed_parts = [time_calls(lambda i: app5(), args.steps),
+                   time_calls(lambda i: dec5(), args.steps)]
     pf_avg_s = pf_b2b_ms / 1e3
     pf_tflops = prefill_flops(w5) / pf_avg_s / 1e12
     del r5
@@ -767,6 +785,16 @@ def main(argv=None):
             "bytes": app_bytes,
             "avg_us": round(statistics.mean(app_ms) * 1e3, 2),
             "GBps": round(app_bytes / (statistics.mean(app_ms) / 1e3) / 1e9, 1),
+        },
+        "mixed_step": {
+            "workload": "qwen2.5-0.5b-shaped continuous-batch step: kv_append of 2108 new tokens, "
+                        "prefill of 4 prompts x 512, decode of 60 sequences with contexts "
+                        "U[64,2048], one stream",
+            "decode_kv_bytes": kv_bytes(w5),
+            "avg_us": round(mixed_ms * 1e3, 2),
+            "append_avg_us": round(mixed_parts[0] * 1e3, 2),
+            "prefill_avg_us": round(pf_b2b_ms * 1e3, 2),
+            "decode_avg_us": round(mixed_parts[1] * 1e3, 2),
         },
         "blocks": blocks,
         "prefill": {

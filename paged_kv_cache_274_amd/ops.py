@@ -160,6 +160,26 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tens
         raise PkvError("kv_append", rc)
 
 
+def bind_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor):
+    """kv_append with its arguments checked and marshalled once: returns a call
+    that launches it (on the stream current now)."""
+    kv_append(k_new[:0], v_new[:0], slot_mapping[:0], k_cache, v_cache)   # the checks
+    n_blocks, h_kv, d = _pool_shape(k_cache, v_cache)
+    _need(k_new.shape[0] == slot_mapping.shape[0] and v_new.shape == k_new.shape,
+          "k_new/v_new/slot_mapping lengths differ")
+    fn = lib().kv_append
+    args = (k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
+            v_cache.data_ptr(), int(k_new.shape[0]), h_kv, d, n_blocks, _DTYPE[k_cache.dtype],
+            _stream(k_cache))
+
+    def call() -> None:
+        rc = fn(*args)
+        if rc != 0:
+            raise PkvError("kv_append", rc)
+    return call
+
+
 def decode_num_splits(B: int, h_q: int, h_kv: int, d_h: int, max_context_len: int,
                       dtype: torch.dtype = torch.bfloat16, num_splits: int = 0) -> int:
     """dtype: the pool's (torch.int8 for the INT8 cache)."""
@@ -275,6 +295,34 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     if rc != 0:
         raise PkvError("paged_decode_attention", rc)
     return out
+
+
+def bind_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                out: torch.Tensor, workspace: torch.Tensor, scale: Optional[float] = None,
+                num_splits: int = 0):
+    """paged_decode_attention with its arguments checked and marshalled once
+    (the first launch runs through the checked call): returns a call that
+    launches it again on the same buffers (on the stream current now)."""
+    paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                           scale=scale, num_splits=num_splits, out=out, workspace=workspace)
+    n_blocks, h_kv, d = _pool_shape(k_cache, v_cache)
+    B, h_q = int(q.shape[0]), int(q.shape[1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    fn = lib().paged_decode_attention
+    args = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), B, h_q, h_kv, d, n_blocks,
+            int(block_tables.shape[1]), int(max_context_len), float(scale), _DTYPE[q.dtype],
+            int(num_splits), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream(q))
+
+    def call() -> torch.Tensor:
+        rc = fn(*args)
+        if rc != 0:
+            raise PkvError("paged_decode_attention", rc)
+        return out
+    return call
 
 
 def paged_prefill_attention(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache: torch.Tensor,

@@ -1,10 +1,12 @@
 /*
  * pkv.h - attention over a block-paged KV cache on AMD MI355X (gfx950).
  *
- * C ABI of libpkv.so.  Every entry point takes plain pointers and sizes, enqueues
- * its kernels on the caller's HIP stream and returns at once.  The library
- * allocates no device memory and keeps no state between calls; it is safe to
- * call from several threads on distinct buffers.
+ * C ABI of libpkv.so.  Every kernel entry point takes plain pointers and sizes,
+ * enqueues its kernels on the caller's HIP stream and returns at once.  The
+ * library allocates no device memory and its kernel entry points keep no state
+ * between calls; they are safe to call from several threads on distinct
+ * buffers.  The block manager (pkv_bm_*) is host-only state in a handle the
+ * caller creates and destroys.
  *
  * Common conventions
  *   - "device" pointers are HIP device (or managed) memory; every tensor is

@@ -394,6 +394,24 @@ def test_batch_append_copies_for_forked_siblings_once():
     assert small.stats() == before and small_l.stats()["free_blocks"] == 1
 
 
+def test_block_tables_export():
+    bm = ops.BlockManager(16, 4)
+    bm.add_sequence(1, list(range(40)))            # 3 blocks
+    bm.add_sequence(2, list(range(100, 110)))      # 1 block
+    tb, ln = bm.block_tables([2, 1])
+    assert tb.shape == (2, 3) and list(ln) == [10, 40]
+    assert list(tb[0]) == [3, 0, 0] and list(tb[1]) == [0, 1, 2]
+    tb, ln = bm.block_tables([1], max_blocks=5)
+    assert list(tb[0]) == [0, 1, 2, 0, 0]
+    with pytest.raises(ops.PkvError):
+        bm.block_tables([1], max_blocks=2)          # too narrow
+    with pytest.raises(ops.PkvError):
+        bm.block_tables([7])                        # unknown
+    bm.swap_out(2)
+    with pytest.raises(ops.PkvError):
+        bm.block_tables([1, 2], max_blocks=4)       # swapped out
+
+
 def test_library_errors():
     bm = ops.BlockManager(4, 1)
     with pytest.raises(ValueError):

@@ -347,3 +347,35 @@ def test_append_skips_negative_slots_and_keeps_other_bits():
                          kc.double().numpy(), vc.double().numpy())
     assert torch.equal(bits(gk.cpu()), bits(torch.from_numpy(ko).to(torch.bfloat16)))
     assert torch.equal(bits(gv.cpu()), bits(torch.from_numpy(vo).to(torch.bfloat16)))
+
+
+def test_bound_calls_match_the_checked_calls():
+    """The pre-bound launches the bench times (bind_kv_append, bind_decode,
+    bind_prefill) give bit for bit what the checked calls give."""
+    w = W.config(5, poison=True)
+    dev = DEV
+    pools = [(w.k_cache.to(dev), w.v_cache.to(dev)) for _ in range(2)]
+    k_new, v_new, slots = w.k_new.to(dev), w.v_new.to(dev), w.slot_mapping.to(dev)
+    q, tbl, lens = w.dec_q.to(dev), w.dec_block_tables.to(dev), w.dec_context_lens.to(dev)
+    ops.kv_append(k_new, v_new, slots, *pools[0])
+    ops.bind_kv_append(k_new, v_new, slots, *pools[1])()
+    ws = torch.empty(ops.decode_workspace_bytes(w.B, w.h_q, w.h_kv, w.d, w.dec_max_context_len),
+                     dtype=torch.uint8, device=dev)
+    out_a = ops.paged_decode_attention(q, *pools[0], tbl, lens, w.dec_max_context_len,
+                                       scale=w.scale)
+    out_b = torch.empty_like(q)
+    dec = ops.bind_decode(q, *pools[1], tbl, lens, w.dec_max_context_len, out_b, ws,
+                          scale=w.scale)
+    out_b.zero_()
+    dec()
+    pre_a = ops.paged_prefill_attention(w.pre_q.to(dev), w.pre_cu_seqlens.to(dev), *pools[0],
+                                        w.pre_block_tables.to(dev), w.pre_context_lens.to(dev),
+                                        w.pre_max_q_len, scale=w.scale)
+    pre_b = ops.bind_prefill(w.pre_q.to(dev), w.pre_cu_seqlens.to(dev), *pools[1],
+                             w.pre_block_tables.to(dev), w.pre_context_lens.to(dev),
+                             w.pre_max_q_len, scale=w.scale)()
+    torch.cuda.synchronize()
+    for a, b in zip(pools[0], pools[1]):
+        assert torch.equal(bits(a.cpu()), bits(b.cpu()))
+    assert torch.equal(bits(out_a.cpu()), bits(out_b.cpu()))
+    assert torch.equal(bits(pre_a.cpu()), bits(pre_b.cpu()))

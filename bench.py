@@ -25,8 +25,8 @@ Printed as one JSON line:
              still match the ones it was taken on
   prefill    paged_prefill_attention on the mixed Qwen2.5-0.5B-shaped batch
              (4 prompts x 512 tokens, h_q=14, h_kv=2, d_h=64) in TFLOP/s
-  verify_decode  the chunked-prefill call with 4 new tokens per config-3
-             sequence (a speculative verify step), in KV GB/s
+  verify_decode  the chunked-prefill call with 4 new tokens per sequence of the
+             decode batch (a speculative verify step), in KV GB/s
   int8_decode  paged_decode_attention_int8 on the same decode step over an
              INT8 cache: bytes = sum_b L_b * 2 * h_kv * (d_h + 4) (codes and
              one float32 scale per token head row), time over back-to-back
@@ -648,7 +648,7 @@ def main(argv=None):
         return 0
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the per-GPU workload is already one GPU's share); run with --gpus 1",
               file=sys.stderr)
         return 2
@@ -682,7 +682,7 @@ def main(argv=None):
     torch.cuda.empty_cache()
 
     # multi-token decode (a speculative verify step): the 4 newest tokens of each
-    # config-3 sequence attend causally over its whole cache, through the
+    # sequence of the decode batch attend causally over its whole cache, through the
     # chunked-prefill call
     wv = W.build("verify", np.random.default_rng(274003), dtype="bf16", h_q=wk.h_q,
                  h_kv=wk.h_kv, d=wk.d, decode_lens=[],
@@ -773,7 +773,7 @@ def main(argv=None):
             "append_avg_us": round(i8_app_ms * 1e3, 2),
         },
         "verify_decode": {
-            "workload": "multi-token decode: the 4 newest tokens of each of the 64 config-3 "
+            "workload": "multi-token decode: the 4 newest tokens of each of the decode batch's 64 "
                         "sequences attend causally over their caches (chunked-prefill call)",
             "kv_bytes": kvbv,
             "avg_us": round(v_ms * 1e3, 2),

@@ -536,12 +536,14 @@ def summarize_stats(stats_csv, bench_json, extra):
         for r in csv.DictReader(f):
             if "pkv::" in r["Name"]:
                 rows.append(r)
-    # the bf16 decode call (the roofline's); the INT8 leg's kernels are listed apart
-    is_bf16 = lambda r: "bf16_t" in r["Name"]  # noqa: E731
+    # the bf16 decode call of the timed batch (the roofline's); the INT8 leg's
+    # kernels, and the decode of the mixed step (d_h = 64), are listed apart
+    d_h = W.config(3 if "--config" not in extra else int(extra.split()[-1])).d
+    is_bf16 = lambda r: f"bf16_t, {d_h}," in r["Name"]  # noqa: E731
     split = [r for r in rows if "decode_split_kernel" in r["Name"] and is_bf16(r)]
     comb = [r for r in rows if "decode_combine_kernel" in r["Name"] and is_bf16(r)]
     call_ns = sum(float(r["AverageNs"]) for r in split + comb)
-    i8 = [r for r in rows if "decode_" in r["Name"] and "i8_t" in r["Name"]]
+    i8 = [r for r in rows if "decode_" in r["Name"] and f"i8_t, {d_h}," in r["Name"]]
     i8_ns = sum(float(r["AverageNs"]) for r in i8)
     text = [
         f"# Kernel time of the benchmark run ({line['config']['workload']})",

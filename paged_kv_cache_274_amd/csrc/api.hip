@@ -238,7 +238,7 @@ static bool decode_shape_ok(int B, int h_q, int h_kv, int max_context_len, int n
 // Automatic split count: one range per wavefront the device holds at once.
 static int auto_splits(int B, int h_q, int h_kv, int d_h, int max_context_len, pkv::KvType kv) {
   const bool bf16 = chunks_as_bf16(kv);
-  const int gc = pkv::head_chunks(h_q / h_kv, d_h, bf16).per_chunk;
+  const int gc = pkv::head_chunks(h_q / h_kv, d_h, bf16, B, h_kv, max_context_len).per_chunk;
   int waves = pkv::decode_resident_waves(d_h, kv, gc);
   if (waves <= 0) waves = 2048;
   const int64_t bound = pkv::decode_split_bound(B, h_q, h_kv, d_h, bf16, max_context_len, 0);
@@ -281,7 +281,7 @@ static int decode_call(void* out, const void* q, const void* k_cache, const void
   if (B == 0) return PKV_OK;
   const bool i8 = kv == pkv::KvType::kI8;
   const bool bf16 = chunks_as_bf16(kv);
-  const pkv::HeadChunks hc = pkv::head_chunks(h_q / h_kv, d_h, bf16);
+  const pkv::HeadChunks hc = pkv::head_chunks(h_q / h_kv, d_h, bf16, B, h_kv, max_context_len);
   if ((int64_t)B * h_kv * hc.n_chunks > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens ||
       (i8 && (!k_scale || !v_scale)))

@@ -114,6 +114,10 @@ def test_prefill_validation():
 def test_workspace_bound(B, h_q, h_kv, d, maxc, dtype):
     g = h_q // h_kv
     cap = 4 if (dtype == torch.float32 and d == 128) else 8
+    # small lines (at most 16 blocks per wave of 2048 at 4-head chunks) take
+    # chunks of at most 4 heads
+    if g > 4 and cap > 4 and B * h_kv * -(-g // 4) * -(-maxc // 16) <= 2048 * 16:
+        cap = 4
     n_chunks = -(-g // cap)
     gc = -(-g // n_chunks)
     upper = B * h_kv * n_chunks * (-(-maxc // 16))

@@ -69,6 +69,23 @@ DECODE_GRID = [
 ]
 
 
+@pytest.mark.parametrize("dtype,d,h_q,h_kv", [("bf16", 64, 14, 2), ("f32", 64, 16, 2),
+                                              ("bf16", 128, 16, 1)])
+def test_decode_large_batch_keeps_wide_chunks(dtype, d, h_q, h_kv):
+    """Small lines split a GQA group of more than 4 heads into chunks of at
+    most 4 (the grid above); large ones keep chunks of up to 8 heads per wave.
+    These batches are large enough for the wide chunks, and match the oracle."""
+    rng = np.random.default_rng(3000 + h_q + d)
+    lens = [int(x) for x in rng.integers(1000, 4096, size=64, endpoint=True)]
+    g = h_q // h_kv
+    assert 64 * h_kv * -(-g // 4) * -(-max(lens) // 16) > 2048 * 16   # above the small-line rule
+    w = W.build("wide", rng, dtype=dtype, h_q=h_q, h_kv=h_kv, d=d, decode_lens=lens,
+                free_frac=0.05, poison=True)
+    res = run(w, DEV)
+    kc_ref, vc_ref = check_append(w, res)
+    check_decode(w, res, kc_ref, vc_ref)
+
+
 @pytest.mark.parametrize("dtype,d,h_q,h_kv", DECODE_GRID)
 @pytest.mark.parametrize("splits", [0, 1, 13, 300])
 def test_decode_grid(dtype, d, h_q, h_kv, splits):

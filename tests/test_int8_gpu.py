@@ -111,6 +111,25 @@ def test_decode_int8_grid(d, h_q, h_kv, splits):
     assert err <= TOL, f"int8 decode max|err| {err}"
 
 
+@pytest.mark.parametrize("d,h_q,h_kv", [(64, 14, 2), (128, 16, 1)])
+def test_decode_int8_large_batch_keeps_wide_chunks(d, h_q, h_kv):
+    """Large batches keep chunks of up to 8 heads per wave (the grid above is
+    small enough for 4-head chunks); the INT8 decode matches the oracle there
+    too."""
+    rng = np.random.default_rng(4000 + h_q + d)
+    lens = [int(x) for x in rng.integers(1000, 4096, size=64, endpoint=True)]
+    g = h_q // h_kv
+    assert 64 * h_kv * -(-g // 4) * -(-max(lens) // 16) > 2048 * 16   # above the small-line rule
+    w = W.build("wide8", rng, dtype="bf16", h_q=h_q, h_kv=h_kv, d=d, decode_lens=lens,
+                free_frac=0.05, poison=True)
+    pools = W.int8_pools(w, seed=12, poison=True)
+    got, ref = _append(w, pools)
+    _check_append_exact(got, ref)
+    out = _decode(w, [t.to(DEV) for t in got])
+    err = max_err(out, _oracle_decode(w, ref))
+    assert err <= TOL, f"int8 decode max|err| {err}"
+
+
 @pytest.mark.parametrize("k", [3, 5])
 def test_decode_int8_configs(k):
     """The decode legs of configs 3 and 5 with an INT8 cache, full size."""

@@ -198,3 +198,28 @@ def test_copy_on_write_then_append_and_decode():
     assert err <= 2e-2
     # the two sequences now differ only in their newest token
     assert not np.allclose(ref[0], ref[1])
+
+
+def test_binding_rejects_malformed_pool_sets():
+    """Argument errors of the bindings are raised before any launch."""
+    a = torch.zeros((8, 2, 16, 64), dtype=torch.bfloat16, device=DEV)
+    b = torch.zeros((9, 2, 16, 64), dtype=torch.bfloat16, device=DEV)
+    pairs = torch.tensor([[0, 1]], dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):
+        ops.copy_blocks([a, b], pairs)                          # block counts differ
+    with pytest.raises(ValueError):
+        ops.copy_blocks([a], pairs.to(torch.int64))             # pairs must be int32
+    with pytest.raises(ValueError):
+        ops.copy_blocks([a], pairs.reshape(2))                  # pairs must be [n, 2]
+    with pytest.raises(ValueError):
+        ops.copy_blocks([a] * 9, pairs)                         # at most 8 pools
+    with pytest.raises(ValueError):
+        ops.copy_blocks([a.cpu()], pairs)                       # pageable host pool
+    h = torch.zeros((4, 2, 16, 32), dtype=torch.bfloat16).pin_memory()
+    with pytest.raises(ValueError):
+        ops.swap_blocks([a], [h], pairs)                        # block shapes differ
+    with pytest.raises(ValueError):
+        ops.swap_blocks([a, a], [b], pairs)                     # set sizes differ
+    with pytest.raises(ops.PkvError):
+        ops.swap_blocks([a], [a], pairs)                        # a pool onto itself
+    torch.cuda.synchronize()

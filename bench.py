@@ -31,6 +31,8 @@ Printed as one JSON line:
              INT8 cache: bytes = sum_b L_b * 2 * h_kv * (d_h + 4) (codes and
              one float32 scale per token head row), time over back-to-back
              calls, and kv_append_int8 of the step's new tokens
+  long_context  decode calls on the long-context batch with a shared prefix
+             (B=8, L=8192, 13 shared blocks), logical and unique KV bytes
   mixed_step the whole continuous-batch step of the Qwen2.5-0.5B-shaped
              workload (append, prefill, decode on one stream), with its parts
   blocks     copy_blocks (copy on write inside a device pool set) and
@@ -695,6 +697,17 @@ def main(argv=None):
     del rv
     torch.cuda.empty_cache()
 
+    # the long-context batch with a shared prefix (8 sequences of 8192 tokens,
+    # 13 shared blocks), decode calls back to back over rotated pool copies
+    if args.config == 3:
+        w4 = W.config(4)
+        r4 = Resident(w4, dev, copies=args.copies)
+        l_ms = time_calls(r4.decode, args.steps, warmup=5)
+        kvb4 = kv_bytes(w4)
+        uniq4 = w4.n_blocks * 16 * 2 * w4.h_kv * w4.d * w4.elem_bytes
+        del r4
+        torch.cuda.empty_cache()
+
     w5 = W.config(5)
     r5 = Resident(w5, dev)
     r5.append(0)
@@ -787,6 +800,15 @@ def main(argv=None):
             "bytes": app_bytes,
             "avg_us": round(statistics.mean(app_ms) * 1e3, 2),
             "GBps": round(app_bytes / (statistics.mean(app_ms) / 1e3) / 1e9, 1),
+        },
+        "long_context": None if args.config != 3 else {
+            "workload": WORKLOAD[4],
+            "kv_bytes": kvb4,
+            "unique_kv_bytes": uniq4,
+            "avg_us": round(l_ms * 1e3, 2),
+            "GBps": round(kvb4 / (l_ms / 1e3) / 1e9, 1),
+            "unique_GBps": round(uniq4 / (l_ms / 1e3) / 1e9, 1),
+            "frac": round(kvb4 / (l_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         },
         "mixed_step": {
             "workload": "qwen2.5-0.5b-shaped continuous-batch step: kv_append of 2108 new tokens, "

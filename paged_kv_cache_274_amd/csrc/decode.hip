@@ -204,10 +204,58 @@ __device__ __forceinline__ int i8_code(const uint2& u, int k) {
 }
 
 // Query registers: bf16 kept packed for v_dot2, fp32 kept as floats (4 words per vector).
+// For an INT8 cache the words become f16 pairs of q * 2^-k (see q_for_codes),
+// with the bias correction of each head and the score factor scale * log2(e) * 2^k.
 template <int GC, int VPL>
 struct QRegs {
   uint32_t w[GC][VPL * 4];
+  float bias[GC];
+  float sfac;
 };
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// INT8 cache: K codes widen to f16 in one byte permutation per pair.  The
+// biased byte u = c + 128 (c ^ 0x80) below an exponent byte 0x64 is the f16
+// value 1024 + u = 1152 + c, exactly, so q . K = q . (1152 + c) - 1152 * sum(q):
+// the scores start from the lane's share of -1152 * sum(q) instead of 0.  The
+// products then need q in f16: q (bf16) is scaled by the power of two 2^-k
+// that brings its largest magnitude over the wave into [2^14, 2^15), which
+// keeps every bf16 value exact in f16 down to 2^-29 of that maximum, and 2^k
+// joins the score factor.  (The widening through float32 conversions costs
+// about twice as many instructions per code; measured on the Llama-3-8B-shaped
+// batch, 77.1 -> 73.8 us per call.)
+// The f16 widening is used for chunks of at most 4 heads: with more, its
+// registers would cost the kernel its second wave per SIMD.
+template <typename T, int GC>
+constexpr bool kF16Codes = std::is_same<T, i8_t>::value && GC <= 4;
+
+template <int GC, int VPL>
+__device__ __forceinline__ void q_for_codes(QRegs<GC, VPL>& q, float scale_log2) {
+  float mx = 0.f;
+#pragma unroll
+  for (int j = 0; j < GC; ++j)
+#pragma unroll
+    for (int x = 0; x < VPL * 4; ++x)
+      mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(q.w[j][x] << 16)),
+                           fabsf(__uint_as_float(q.w[j][x] & 0xffff0000u))));
+  mx = wave_max(mx);
+  const int k = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) - 15 : 0;
+  const float down = __builtin_amdgcn_ldexpf(1.f, -k);
+#pragma unroll
+  for (int j = 0; j < GC; ++j) {
+    float sum = 0.f;
+#pragma unroll
+    for (int x = 0; x < VPL * 4; ++x) {
+      const float lo = __uint_as_float(q.w[j][x] << 16) * down;
+      const float hi = __uint_as_float(q.w[j][x] & 0xffff0000u) * down;
+      sum += lo + hi;
+      q.w[j][x] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    }
+    q.bias[j] = -1152.f * sum;
+  }
+  q.sfac = __builtin_amdgcn_ldexpf(scale_log2, k);
+}
 
 
 
@@ -232,7 +280,7 @@ __device__ __forceinline__ void attend_block(const BlockOf<T, D>& r,
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps)
 #pragma unroll
-    for (int j = 0; j < GC; ++j) s[ps][j] = 0.f;
+    for (int j = 0; j < GC; ++j) s[ps][j] = kF16Codes<T, GC> ? q.bias[j] : 0.f;
 #pragma unroll
   for (int v = 0; v < VPL; ++v)
 #pragma unroll
@@ -240,7 +288,10 @@ __device__ __forceinline__ void attend_block(const BlockOf<T, D>& r,
 #pragma unroll
       for (int ps = 0; ps < NP; ++ps) {
         uint32_t kw;
-        if constexpr (std::is_same<T, i8_t>::value)
+        if constexpr (kF16Codes<T, GC>)
+          kw = __builtin_amdgcn_perm(0x64646464u, ((w < 2) ? r.k[ps].x : r.k[ps].y) ^ 0x80808080u,
+                                     (w & 1) ? 0x04030402u : 0x04010400u);
+        else if constexpr (std::is_same<T, i8_t>::value)
           kw = i8_pair_bf16(i8_code(r.k[ps], 2 * w), i8_code(r.k[ps], 2 * w + 1));
         else
           kw = dw(r.k[ps][v], w);
@@ -248,6 +299,10 @@ __device__ __forceinline__ void attend_block(const BlockOf<T, D>& r,
         for (int j = 0; j < GC; ++j) {
           if constexpr (std::is_same<T, float>::value)
             s[ps][j] = fmaf(__uint_as_float(q.w[j][v * 4 + w]), __uint_as_float(kw), s[ps][j]);
+          else if constexpr (kF16Codes<T, GC>)
+            s[ps][j] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, kw),
+                                              __builtin_bit_cast(f16x2_t, q.w[j][v * 4 + w]),
+                                              s[ps][j], false);
           else
             s[ps][j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kw),
                                                        __builtin_bit_cast(bf16x2_t, q.w[j][v * 4 + w]),
@@ -277,7 +332,8 @@ __device__ __forceinline__ void attend_block(const BlockOf<T, D>& r,
   for (int ps = 0; ps < NP; ++ps) {
     ok[ps] = !MASK || (token_of<T, D>(ps, slot) < valid);
     float f = scale_log2;
-    if constexpr (std::is_same<T, i8_t>::value) f = r.ks[ps] * scale_log2;  // the token's K scale
+    if constexpr (kF16Codes<T, GC>) f = r.ks[ps] * q.sfac;  // the token's K scale
+    else if constexpr (std::is_same<T, i8_t>::value) f = r.ks[ps] * scale_log2;
 #pragma unroll
     for (int j = 0; j < GC; ++j) s[ps][j] = (MASK && !ok[ps]) ? kNegInf : s[ps][j] * f;
   }
@@ -737,6 +793,7 @@ struct RangeStream {
         attend_block<T, D, GC, true>(X, q, m, l, acc, a.scale_log2, slot_id, valid);
     };
 
+    if constexpr (kF16Codes<T, GC>) q_for_codes(q, a.scale_log2);
     // Block t of the current piece is in A, or in B when in_b (a register copy
     // from B to A would wait for that block's loads and drain the pipeline, so
     // the roles swap instead: one step from B realigns the walk to A).
@@ -777,6 +834,7 @@ struct RangeStream {
       for (int j = 0; j < GC; ++j)
 #pragma unroll
         for (int x = 0; x < VPL * 4; ++x) q.w[j][x] = qn.w[j][x];
+      if constexpr (kF16Codes<T, GC>) q_for_codes(q, a.scale_log2);
       reset();
       t = 0;
       ent0 = nxt_blk1;

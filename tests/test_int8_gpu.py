@@ -159,3 +159,21 @@ def test_decode_int8_zero_length_and_split_agreement():
         assert max_err(_decode(w, dev, splits), a.double().numpy()) <= TOL
     # one wave per sequence reduces in a fixed order: repeatable bit for bit
     assert torch.equal(bits(a), bits(_decode(w, dev, 1)))
+
+
+@pytest.mark.parametrize("q_mag", [1e-6, 1.0, 3e5])
+def test_decode_int8_query_magnitudes(q_mag):
+    """The INT8 decode forms K products in f16 from q scaled by a power of two
+    per piece; queries far outside f16's range (3e5, or 1e-6 where f16 would
+    flush them) must still match the oracle."""
+    rng = np.random.default_rng(4100)
+    w = W.build("qmag", rng, dtype="bf16", h_q=16, h_kv=4, d=128,
+                decode_lens=[1, 17, 300, 1000, 2500], free_frac=0.2, poison=True)
+    w.dec_q = (w.dec_q.float() * q_mag).to(torch.bfloat16)
+    pools = W.int8_pools(w, seed=13, poison=True)
+    got, ref = _append(w, pools)
+    _check_append_exact(got, ref)
+    for splits in (0, 7):
+        out = _decode(w, [t.to(DEV) for t in got], splits)
+        err = max_err(out, _oracle_decode(w, ref))
+        assert err <= TOL, f"int8 decode max|err| {err} at |q| ~ {q_mag}"

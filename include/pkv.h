@@ -32,7 +32,7 @@
  *     Verification Code Examples).
  *   - Grouped-query attention (the "GQA" of the Attention Kernel box, pipeline
  *     figure, From Scratch page): query head h reads KV head h / (h_q / h_kv).
- *   - stream: a hipStream_t passed as void*; NULL is the null stream.
+ *   - stream: the HIP stream the work is enqueued on; NULL is the null stream.
  *
  * Errors: every call returns a pkv_status.  Host-checkable argument errors are
  * reported before any HIP call is made and nothing is enqueued.  Values that
@@ -56,9 +56,14 @@
 extern "C" {
 #endif
 
+/* The HIP stream handle, declared exactly as HIP's runtime header declares it
+ * (an identical typedef may be repeated in C11 and C++), so that this header
+ * needs no HIP include. */
+typedef struct ihipStream_t* hipStream_t;
+
 /* PKV_INT8 names the INT8 cache (int8 codes with a float32 scale per token
  * head row, read by bf16 queries); it is accepted by pkv_decode_num_splits and
- * pkv_decode_workspace_bytes only. */
+ * pkv_decode_workspace_bytes_split only. */
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_INT8 = 2 } pkv_dtype;
 
 typedef enum {
@@ -94,7 +99,7 @@ const char* pkv_status_string(int status);
  */
 int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
               void* k_cache, void* v_cache,
-              int T, int h_kv, int d_h, int n_blocks, int dtype, void* stream);
+              int T, int h_kv, int d_h, int n_blocks, int dtype, hipStream_t stream);
 
 /*
  * paged_decode_attention - one query token per sequence attends to its whole
@@ -115,24 +120,51 @@ int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
  *   max_context_len : host int, an upper bound of context_lens,
  *                  0 <= max_context_len <= max_blocks_per_seq * 16.
  *   scale : the softmax scale (1/sqrt(d_h) for standard attention).
- *   num_splits : 0 picks the split automatically (one range per wavefront the
- *                  device holds at once, capped by the work); otherwise the
- *                  number of equal ranges, 1 .. 65536, that the blocks of all
- *                  (sequence, KV head) pairs, laid end to end, are cut into.
- *                  Results agree across splits to rounding.
- *   workspace : device scratch of at least pkv_decode_workspace_bytes(...) bytes
- *                  for the same arguments, 16-byte aligned.  Its contents on
- *                  entry do not matter.  The caller owns it and must not use it
+ *   workspace : device scratch of at least
+ *                  pkv_decode_workspace_bytes(B, h_q, d_h, max_context_len)
+ *                  bytes, 16-byte aligned.  Its contents on entry do not
+ *                  matter.  The caller owns it and must not use it
  *                  concurrently with the call.
- * B == 0 enqueues nothing.  Requires h_q % h_kv == 0, d_h in {64, 128}.
+ * The blocks of all (sequence, KV head) pairs, laid end to end, are cut into
+ * one equal range per wavefront the device holds at once; results do not
+ * depend on the cut beyond fp32 rounding.  B == 0 enqueues nothing.  Requires
+ * h_q % h_kv == 0, d_h in {64, 128}.
  */
 int paged_decode_attention(void* out, const void* q,
                            const void* k_cache, const void* v_cache,
                            const int32_t* block_tables, const int32_t* context_lens,
                            int B, int h_q, int h_kv, int d_h, int n_blocks,
                            int max_blocks_per_seq, int max_context_len,
-                           float scale, int dtype, int num_splits,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           float scale, int dtype,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes paged_decode_attention needs for these arguments, whatever
+ * h_kv (dividing h_q) and the pool dtype (bf16, fp32 or INT8): an upper bound.
+ * Host-only, no HIP call.  0 for B <= 0 or other invalid arguments. */
+size_t pkv_decode_workspace_bytes(int B, int h_q, int d_h, int max_context_len);
+
+/*
+ * paged_decode_attention_split - paged_decode_attention with the number of
+ * ranges set by the caller (for tuning and for tests of the merge):
+ *   num_splits : 0 picks the split automatically (as paged_decode_attention);
+ *                  otherwise 1 .. 65536 equal ranges.
+ *   workspace : at least pkv_decode_workspace_bytes_split(B, h_q, h_kv, d_h,
+ *                  max_context_len, dtype, num_splits) bytes.
+ */
+int paged_decode_attention_split(void* out, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int B, int h_q, int h_kv, int d_h, int n_blocks,
+                                 int max_blocks_per_seq, int max_context_len,
+                                 float scale, int dtype, int num_splits,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Exact workspace bytes of a decode call with these arguments (dtype PKV_F32,
+ * PKV_BF16 or PKV_INT8; num_splits as for paged_decode_attention_split, 0 =
+ * enough for the largest automatic split).  Host-only, no HIP call.  Returns 0
+ * for invalid arguments; the call itself then reports the error. */
+size_t pkv_decode_workspace_bytes_split(int B, int h_q, int h_kv, int d_h, int max_context_len,
+                                        int dtype, int num_splits);
 
 /*
  * INT8 KV cache.  The cached K and V are quantised dynamically to int8 per
@@ -158,16 +190,17 @@ int paged_decode_attention(void* out, const void* q,
  */
 int kv_append_int8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                    int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale,
-                   int T, int h_kv, int d_h, int n_blocks, int dtype, void* stream);
+                   int T, int h_kv, int d_h, int n_blocks, int dtype, hipStream_t stream);
 
 /*
  * paged_decode_attention_int8 - paged_decode_attention over an INT8 cache:
  * the same result with K and V replaced by x_hat = s * x_q.  q and out are
  * bf16; the codes are widened exactly in registers, the K scale multiplies the
  * score and the V scale the softmax weight (weights rounded to bf16 as in the
- * bf16 decode; accumulation in fp32).  Other arguments and the workspace are
- * as for paged_decode_attention (size it with dtype PKV_INT8, which equals the
- * bf16 size).
+ * bf16 decode; accumulation in fp32).  Other arguments are as for
+ * paged_decode_attention_split; the workspace is sized by
+ * pkv_decode_workspace_bytes (any num_splits == 0 call) or
+ * pkv_decode_workspace_bytes_split with dtype PKV_INT8.
  */
 int paged_decode_attention_int8(void* out, const void* q,
                                 const int8_t* k_cache, const int8_t* v_cache,
@@ -176,20 +209,14 @@ int paged_decode_attention_int8(void* out, const void* q,
                                 int B, int h_q, int h_kv, int d_h, int n_blocks,
                                 int max_blocks_per_seq, int max_context_len, float scale,
                                 int num_splits, void* workspace, size_t workspace_bytes,
-                                void* stream);
+                                hipStream_t stream);
 
-/* Number of splits paged_decode_attention uses for these arguments; -1 on
- * invalid arguments.  With num_splits == 0 it queries the current device's
- * occupancy for the decode kernel (2048 wavefronts are assumed when no device
- * can be queried). */
+/* Number of splits a decode call uses for these arguments; -1 on invalid
+ * arguments.  With num_splits == 0 it queries the current device's occupancy
+ * for the decode kernel (2048 wavefronts are assumed when no device can be
+ * queried). */
 int pkv_decode_num_splits(int B, int h_q, int h_kv, int d_h, int max_context_len, int dtype,
                           int num_splits);
-
-/* Workspace bytes paged_decode_attention needs for these arguments: enough for
- * the largest automatic split.  Host-only, no HIP call.  Returns 0 for invalid
- * arguments; the call itself then reports the error. */
-size_t pkv_decode_workspace_bytes(int B, int h_q, int h_kv, int d_h, int max_context_len,
-                                  int dtype, int num_splits);
 
 /*
  * paged_prefill_attention - causal attention of the new prompt tokens of S
@@ -217,7 +244,7 @@ int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_
                             const int32_t* block_tables, const int32_t* context_lens,
                             int S, int T_q, int max_q_len, int h_q, int h_kv, int d_h,
                             int n_blocks, int max_blocks_per_seq, float scale, int dtype,
-                            void* stream);
+                            hipStream_t stream);
 
 /*
  * Block copies between KV pools.
@@ -251,7 +278,7 @@ int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_
  * a destination in one call (the copies run in parallel).
  */
 int copy_blocks(void* const* pools, const int64_t* block_bytes, int n_pools, int n_blocks,
-                const int32_t* pairs, int n_pairs, void* stream);
+                const int32_t* pairs, int n_pairs, hipStream_t stream);
 
 /*
  * swap_blocks - between two pool sets (device and pinned host, either way, or
@@ -264,7 +291,7 @@ int copy_blocks(void* const* pools, const int64_t* block_bytes, int n_pools, int
  */
 int swap_blocks(const void* const* src_pools, void* const* dst_pools, const int64_t* block_bytes,
                 int n_pools, int n_src_blocks, int n_dst_blocks, const int32_t* pairs,
-                int n_pairs, void* stream);
+                int n_pairs, hipStream_t stream);
 
 /*
  * Block manager (host-only; no HIP call).  It decides which physical block of a

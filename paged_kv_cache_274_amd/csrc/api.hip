@@ -121,7 +121,7 @@ int debug_check_pairs(const int32_t* pairs, int n_pairs, int n_src, int n_dst, b
 // Both block-copy entry points.  src == dst for a copy within one pool set.
 int copy_call(const void* const* src, void* const* dst, const int64_t* block_bytes, int n_pools,
               int n_src, int n_dst, const int32_t* pairs, int n_pairs, bool same_set,
-              void* stream) {
+              hipStream_t stream) {
   if (n_pools < 1 || n_pools > pkv::kMaxCopyPools || n_src < 1 || n_dst < 1 || n_pairs < 0 ||
       !src || !dst || !block_bytes)
     return PKV_ERR_INVALID_ARG;
@@ -151,7 +151,7 @@ int copy_call(const void* const* src, void* const* dst, const int64_t* block_byt
   const void* pairs_dev;
   bool pairs_host;
   if (!device_address(pairs, &pairs_dev, &pairs_host)) return PKV_ERR_INVALID_ARG;
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = stream;
   if (debug_checks()) {
     const int rc = debug_check_pairs(pairs, n_pairs, n_src, n_dst, same_set, s);
     if (rc != PKV_OK) return rc;
@@ -188,7 +188,7 @@ const char* pkv_status_string(int status) {
 }
 
 int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping, void* k_cache,
-              void* v_cache, int T, int h_kv, int d_h, int n_blocks, int dtype, void* stream) {
+              void* v_cache, int T, int h_kv, int d_h, int n_blocks, int dtype, hipStream_t stream) {
   const int eb = elem_bytes(dtype);
   if (eb == 0) return PKV_ERR_INVALID_ARG;
   if (T < 0 || h_kv <= 0 || n_blocks <= 0) return PKV_ERR_INVALID_ARG;
@@ -198,7 +198,7 @@ int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
       ((uintptr_t)slot_mapping & 7u))
     return PKV_ERR_INVALID_ARG;
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = stream;
   if (debug_checks()) {
     const int rc = debug_check_slots(slot_mapping, T, n_blocks, s);
     if (rc != PKV_OK) return rc;
@@ -209,7 +209,7 @@ int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
 
 int kv_append_int8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                    int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale, int T,
-                   int h_kv, int d_h, int n_blocks, int dtype, void* stream) {
+                   int h_kv, int d_h, int n_blocks, int dtype, hipStream_t stream) {
   const int eb = elem_bytes(dtype);
   if (eb == 0) return PKV_ERR_INVALID_ARG;
   if (T < 0 || h_kv <= 0 || n_blocks <= 0) return PKV_ERR_INVALID_ARG;
@@ -221,7 +221,7 @@ int kv_append_int8(const void* k_new, const void* v_new, const int64_t* slot_map
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
       ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u) || ((uintptr_t)slot_mapping & 7u))
     return PKV_ERR_INVALID_ARG;
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = stream;
   if (debug_checks()) {
     const int rc = debug_check_slots(slot_mapping, T, n_blocks, s);
     if (rc != PKV_OK) return rc;
@@ -255,14 +255,19 @@ int pkv_decode_num_splits(int B, int h_q, int h_kv, int d_h, int max_context_len
   return auto_splits(B, h_q, h_kv, d_h, max_context_len, kv);
 }
 
-size_t pkv_decode_workspace_bytes(int B, int h_q, int h_kv, int d_h, int max_context_len,
-                                  int dtype, int num_splits) {
+size_t pkv_decode_workspace_bytes_split(int B, int h_q, int h_kv, int d_h, int max_context_len,
+                                        int dtype, int num_splits) {
   pkv::KvType kv;
   if (!decode_shape_ok(B, h_q, h_kv, max_context_len, num_splits) || d_h <= 0 ||
       !kv_type_of(dtype, &kv))
     return 0;
   return pkv::decode_workspace_bytes(B, h_q, h_kv, d_h, chunks_as_bf16(kv), max_context_len,
                                      num_splits);
+}
+
+size_t pkv_decode_workspace_bytes(int B, int h_q, int d_h, int max_context_len) {
+  if (B <= 0 || h_q <= 0 || d_h <= 0 || max_context_len < 0) return 0;
+  return pkv::decode_workspace_bound(B, h_q, d_h, max_context_len);
 }
 
 // Both decode entry points: validation, workspace layout and launch.  k_scale
@@ -272,7 +277,7 @@ static int decode_call(void* out, const void* q, const void* k_cache, const void
                        const int32_t* context_lens, int B, int h_q, int h_kv, int d_h,
                        int n_blocks, int max_blocks_per_seq, int max_context_len, float scale,
                        pkv::KvType kv, int num_splits, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       hipStream_t stream) {
   if (!decode_shape_ok(B, h_q, h_kv, max_context_len, num_splits) || n_blocks <= 0 ||
       max_blocks_per_seq <= 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * 16 ||
       !isfinite(scale))
@@ -293,7 +298,7 @@ static int decode_call(void* out, const void* q, const void* k_cache, const void
   const size_t need =
       pkv::decode_workspace_bytes(B, h_q, h_kv, d_h, bf16, max_context_len, num_splits);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKV_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = stream;
   if (debug_checks()) {
     const int rc = debug_check_tables(block_tables, context_lens, B, max_blocks_per_seq,
                                       max_context_len, n_blocks, s);
@@ -325,11 +330,12 @@ static int decode_call(void* out, const void* q, const void* k_cache, const void
   return from_hip(pkv::launch_decode(a, d_h, kv, s));
 }
 
-int paged_decode_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
-                           const int32_t* block_tables, const int32_t* context_lens, int B,
-                           int h_q, int h_kv, int d_h, int n_blocks, int max_blocks_per_seq,
-                           int max_context_len, float scale, int dtype, int num_splits,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+int paged_decode_attention_split(void* out, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, int B, int h_q, int h_kv, int d_h,
+                                 int n_blocks, int max_blocks_per_seq, int max_context_len,
+                                 float scale, int dtype, int num_splits, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
   if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
   return decode_call(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, B,
                      h_q, h_kv, d_h, n_blocks, max_blocks_per_seq, max_context_len, scale,
@@ -337,12 +343,23 @@ int paged_decode_attention(void* out, const void* q, const void* k_cache, const 
                      workspace, workspace_bytes, stream);
 }
 
+int paged_decode_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, int B,
+                           int h_q, int h_kv, int d_h, int n_blocks, int max_blocks_per_seq,
+                           int max_context_len, float scale, int dtype, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  return paged_decode_attention_split(out, q, k_cache, v_cache, block_tables, context_lens, B,
+                                      h_q, h_kv, d_h, n_blocks, max_blocks_per_seq,
+                                      max_context_len, scale, dtype, 0, workspace,
+                                      workspace_bytes, stream);
+}
+
 int paged_decode_attention_int8(void* out, const void* q, const int8_t* k_cache,
                                 const int8_t* v_cache, const float* k_scale, const float* v_scale,
                                 const int32_t* block_tables, const int32_t* context_lens, int B,
                                 int h_q, int h_kv, int d_h, int n_blocks, int max_blocks_per_seq,
                                 int max_context_len, float scale, int num_splits, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                size_t workspace_bytes, hipStream_t stream) {
   return decode_call(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, B,
                      h_q, h_kv, d_h, n_blocks, max_blocks_per_seq, max_context_len, scale,
                      pkv::KvType::kI8, num_splits, workspace, workspace_bytes, stream);
@@ -352,7 +369,7 @@ int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_
                             const void* k_cache, const void* v_cache, const int32_t* block_tables,
                             const int32_t* context_lens, int S, int T_q, int max_q_len, int h_q,
                             int h_kv, int d_h, int n_blocks, int max_blocks_per_seq, float scale,
-                            int dtype, void* stream) {
+                            int dtype, hipStream_t stream) {
   if (elem_bytes(dtype) == 0) return PKV_ERR_INVALID_ARG;
   if (S < 0 || T_q < 0 || max_q_len < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0 ||
       n_blocks <= 0 || max_blocks_per_seq <= 0 || !isfinite(scale))
@@ -367,7 +384,7 @@ int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_
       ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u) ||
       ((uintptr_t)cu_seqlens_q & 3u))
     return PKV_ERR_INVALID_ARG;
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = stream;
   if (debug_checks()) {
     std::vector<int32_t> cu, l;
     if (!copy_to_host(cu, cu_seqlens_q, (size_t)S + 1, s)) return PKV_ERR_HIP;
@@ -402,14 +419,14 @@ int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_
 }
 
 int copy_blocks(void* const* pools, const int64_t* block_bytes, int n_pools, int n_blocks,
-                const int32_t* pairs, int n_pairs, void* stream) {
+                const int32_t* pairs, int n_pairs, hipStream_t stream) {
   return copy_call((const void* const*)pools, pools, block_bytes, n_pools, n_blocks, n_blocks,
                    pairs, n_pairs, true, stream);
 }
 
 int swap_blocks(const void* const* src_pools, void* const* dst_pools, const int64_t* block_bytes,
                 int n_pools, int n_src_blocks, int n_dst_blocks, const int32_t* pairs,
-                int n_pairs, void* stream) {
+                int n_pairs, hipStream_t stream) {
   return copy_call(src_pools, dst_pools, block_bytes, n_pools, n_src_blocks, n_dst_blocks, pairs,
                    n_pairs, false, stream);
 }

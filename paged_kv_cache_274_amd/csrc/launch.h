@@ -83,6 +83,21 @@ inline size_t decode_workspace_bytes(int B, int h_q, int h_kv, int d_h, bool bf1
          ((segs * 2 * sizeof(int32_t) + 15) / 16) * 16 + 16;
 }
 
+// Workspace bound that needs neither h_kv nor the dtype: for any h_kv dividing
+// h_q and any pool type, the automatic split count is at most
+// min(kMaxAutoSplits, B * h_q * ceil(L / 16)) (a segment holds at least one
+// query head, so there are at most B * h_q segments), a chunk holds at most
+// min(8, h_q) heads, and there are at most B * h_q segment descriptors.
+inline size_t decode_workspace_bound(int B, int h_q, int d_h, int max_context_len) {
+  if (B <= 0) return 0;
+  const int64_t segs = (int64_t)B * h_q;
+  int64_t splits = segs * ((max_context_len + 15) / 16);
+  splits = splits < 1 ? 1 : (splits > kMaxAutoSplits ? kMaxAutoSplits : splits);
+  const int gc = h_q < 8 ? h_q : 8;
+  return (size_t)splits * 2 * gc * (size_t)(d_h + 2) * sizeof(float) +
+         (((size_t)segs * 2 * sizeof(int32_t) + 15) / 16) * 16 + 16;
+}
+
 // Element type of a KV pool.  kI8: int8 codes with a float32 scale per token
 // head row, read by bf16 queries.
 enum class KvType { kF32, kBF16, kI8 };

@@ -24,6 +24,7 @@ _WS_DTYPE = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.int8: PKV_I
 EXPORTED = ("kv_append", "paged_decode_attention", "paged_prefill_attention",
             "kv_append_int8", "paged_decode_attention_int8",
             "pkv_decode_workspace_bytes", "pkv_decode_num_splits", "pkv_status_string",
+            "paged_decode_attention_split", "pkv_decode_workspace_bytes_split",
             "copy_blocks", "swap_blocks",
             "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_sequence", "pkv_bm_append",
             "pkv_bm_fork", "pkv_bm_free", "pkv_bm_swap_out", "pkv_bm_swap_in",
@@ -69,11 +70,17 @@ def lib() -> ctypes.CDLL:
     L.kv_append.restype = i32
     L.pkv_decode_num_splits.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.pkv_decode_num_splits.restype = i32
-    L.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.pkv_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.pkv_decode_workspace_bytes_split.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.pkv_decode_workspace_bytes_split.restype = ctypes.c_size_t
     L.paged_decode_attention.argtypes = [vp, vp, vp, vp, i32p, i32p, i32, i32, i32, i32, i32, i32,
-                                         i32, ctypes.c_float, i32, i32, vp, ctypes.c_size_t, vp]
+                                         i32, ctypes.c_float, i32, vp, ctypes.c_size_t, vp]
     L.paged_decode_attention.restype = i32
+    L.paged_decode_attention_split.argtypes = [vp, vp, vp, vp, i32p, i32p, i32, i32, i32, i32,
+                                               i32, i32, i32, ctypes.c_float, i32, i32, vp,
+                                               ctypes.c_size_t, vp]
+    L.paged_decode_attention_split.restype = i32
     L.paged_prefill_attention.argtypes = [vp, vp, i32p, vp, vp, i32p, i32p, i32, i32, i32, i32, i32,
                                           i32, i32, i32, ctypes.c_float, i32, vp]
     L.paged_prefill_attention.restype = i32
@@ -189,9 +196,16 @@ def decode_num_splits(B: int, h_q: int, h_kv: int, d_h: int, max_context_len: in
 
 def decode_workspace_bytes(B: int, h_q: int, h_kv: int, d_h: int, max_context_len: int,
                            dtype: torch.dtype = torch.bfloat16, num_splits: int = 0) -> int:
-    """dtype: the pool's (torch.int8 for the INT8 cache)."""
-    return int(lib().pkv_decode_workspace_bytes(B, h_q, h_kv, d_h, max_context_len,
-                                                 _WS_DTYPE[dtype], num_splits))
+    """Exact workspace of a decode call (pkv_decode_workspace_bytes_split).
+    dtype: the pool's (torch.int8 for the INT8 cache)."""
+    return int(lib().pkv_decode_workspace_bytes_split(B, h_q, h_kv, d_h, max_context_len,
+                                                       _WS_DTYPE[dtype], num_splits))
+
+
+def decode_workspace_bound(B: int, h_q: int, d_h: int, max_context_len: int) -> int:
+    """Workspace that serves any automatic-split decode call of these sizes,
+    whatever h_kv and dtype (pkv_decode_workspace_bytes)."""
+    return int(lib().pkv_decode_workspace_bytes(B, h_q, d_h, max_context_len))
 
 
 def _scale_pools(k_scale: torch.Tensor, v_scale: torch.Tensor, n_blocks: int, h_kv: int):
@@ -287,14 +301,25 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = lib().paged_decode_attention(
-        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-        block_tables.data_ptr(), context_lens.data_ptr(), B, h_q, h_kv, d, n_blocks,
-        int(block_tables.shape[1]), int(max_context_len), float(scale), _DTYPE[q.dtype],
-        int(num_splits), ws_ptr, ws_len, _stream(q))
+    fn, args = _decode_launch(out, q, k_cache, v_cache, block_tables, context_lens, B, h_q, h_kv,
+                              d, n_blocks, max_context_len, scale, num_splits, ws_ptr, ws_len)
+    rc = fn(*args)
     if rc != 0:
         raise PkvError("paged_decode_attention", rc)
     return out
+
+
+def _decode_launch(out, q, k_cache, v_cache, block_tables, context_lens, B, h_q, h_kv, d,
+                   n_blocks, max_context_len, scale, num_splits, ws_ptr, ws_len):
+    """The C entry point and its arguments: paged_decode_attention for the
+    automatic split, paged_decode_attention_split for an explicit count."""
+    head = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), B, h_q, h_kv, d, n_blocks,
+            int(block_tables.shape[1]), int(max_context_len), float(scale), _DTYPE[q.dtype])
+    tail = (ws_ptr, ws_len, _stream(q))
+    if int(num_splits) == 0:
+        return lib().paged_decode_attention, head + tail
+    return lib().paged_decode_attention_split, head + (int(num_splits),) + tail
 
 
 def bind_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -310,12 +335,9 @@ def bind_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     B, h_q = int(q.shape[0]), int(q.shape[1])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    fn = lib().paged_decode_attention
-    args = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-            block_tables.data_ptr(), context_lens.data_ptr(), B, h_q, h_kv, d, n_blocks,
-            int(block_tables.shape[1]), int(max_context_len), float(scale), _DTYPE[q.dtype],
-            int(num_splits), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-            _stream(q))
+    fn, args = _decode_launch(out, q, k_cache, v_cache, block_tables, context_lens, B, h_q, h_kv,
+                              d, n_blocks, max_context_len, scale, num_splits,
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size())
 
     def call() -> torch.Tensor:
         rc = fn(*args)

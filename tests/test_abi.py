@@ -59,10 +59,23 @@ def test_kv_append_validation():
 
 
 def _decode(**kw):
+    """paged_decode_attention with exactly the boundary's argument list: out, q,
+    k_cache, v_cache, block_tables, context_lens, B, h_q, h_kv, d_h, n_blocks,
+    max_blocks_per_seq, max_context_len, scale, dtype, workspace,
+    workspace_bytes, stream."""
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, tbl=FAKE, lens=FAKE, B=4, h_q=8, h_kv=2, d=128,
+             nb=64, mb=16, maxc=256, scale=0.1, dt=1, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return ops.lib().paged_decode_attention(
+        a["out"], a["q"], a["kc"], a["vc"], a["tbl"], a["lens"], a["B"], a["h_q"], a["h_kv"],
+        a["d"], a["nb"], a["mb"], a["maxc"], a["scale"], a["dt"], a["ws"], a["ws_bytes"], None)
+
+
+def _decode_split(**kw):
     a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, tbl=FAKE, lens=FAKE, B=4, h_q=8, h_kv=2, d=128,
              nb=64, mb=16, maxc=256, scale=0.1, dt=1, P=0, ws=FAKE, ws_bytes=1 << 30)
     a.update(kw)
-    return ops.lib().paged_decode_attention(
+    return ops.lib().paged_decode_attention_split(
         a["out"], a["q"], a["kc"], a["vc"], a["tbl"], a["lens"], a["B"], a["h_q"], a["h_kv"],
         a["d"], a["nb"], a["mb"], a["maxc"], a["scale"], a["dt"], a["P"], a["ws"], a["ws_bytes"],
         None)
@@ -70,21 +83,48 @@ def _decode(**kw):
 
 def test_decode_validation():
     assert _decode(dt=3) == 1
+    assert _decode(dt=2) == 1           # the INT8 cache has its own entry point
     assert _decode(h_q=6, h_kv=4) == 1
     assert _decode(maxc=16 * 16 + 1) == 1
     assert _decode(B=-1) == 1
     assert _decode(d=80) == 2
     assert _decode(q=None) == 1
     assert _decode(out=MISALIGNED) == 1
-    assert _decode(P=-2) == 1
-    assert _decode(P=(1 << 16) + 1) == 1
     assert _decode(scale=float("nan")) == 1
-    assert _decode(ws=None, P=16) == 3
+    assert _decode(ws=None) == 3
+    exact = ops.decode_workspace_bytes(4, 8, 2, 128, 256)
+    assert _decode(ws_bytes=exact - 1) == 3
+    assert _decode(ws=MISALIGNED) == 3
+    assert _decode(B=0, out=None, q=None) == 0
+
+
+def test_decode_split_validation():
+    assert _decode_split(P=-2) == 1
+    assert _decode_split(P=(1 << 16) + 1) == 1
+    assert _decode_split(ws=None, P=16) == 3
     need = ops.decode_workspace_bytes(4, 8, 2, 128, 256, num_splits=16)
     assert need == 16 * 2 * 4 * 130 * 4 + 4 * 2 * 8 + 16   # partials, segment descriptors, header
-    assert _decode(P=16, ws_bytes=need - 1) == 3
-    assert _decode(ws=MISALIGNED, P=16) == 3
-    assert _decode(B=0, out=None, q=None) == 0
+    assert _decode_split(P=16, ws_bytes=need - 1) == 3
+    assert _decode_split(ws=MISALIGNED, P=16) == 3
+    assert _decode_split(dt=2) == 1
+    assert _decode_split(B=0, out=None, q=None) == 0
+
+
+@pytest.mark.parametrize("B,h_q,d,maxc", [(64, 32, 128, 4096), (8, 32, 128, 8192), (8, 32, 64, 512),
+                                          (60, 14, 64, 2048), (2, 4, 64, 40), (1, 64, 128, 100000),
+                                          (3, 1, 64, 0), (300, 8, 128, 17)])
+def test_boundary_workspace_bound_covers_every_h_kv_and_dtype(B, h_q, d, maxc):
+    """pkv_decode_workspace_bytes(B, h_q, d_h, max_context_len) knows neither
+    h_kv nor the dtype: it must cover the exact automatic-split workspace of
+    every h_kv dividing h_q and every pool dtype, and a call given exactly that
+    many bytes must pass the workspace check."""
+    bound = ops.lib().pkv_decode_workspace_bytes(B, h_q, d, maxc)
+    assert bound > 0
+    for h_kv in [h for h in range(1, h_q + 1) if h_q % h == 0]:
+        for dt in (torch.float32, torch.bfloat16, torch.int8):
+            assert ops.decode_workspace_bytes(B, h_q, h_kv, d, maxc, dt) <= bound, (h_kv, dt)
+    assert ops.lib().pkv_decode_workspace_bytes(0, h_q, d, maxc) == 0
+    assert ops.lib().pkv_decode_workspace_bytes(B, h_q, d, -1) == 0
 
 
 def _prefill(**kw):
@@ -172,7 +212,7 @@ def test_decode_int8_validation():
         assert (ops.decode_workspace_bytes(4, 8, 2, 128, 256, torch.int8, n) ==
                 ops.decode_workspace_bytes(4, 8, 2, 128, 256, torch.bfloat16, n))
     assert ops.lib().paged_decode_attention(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 2, 128, 64,
-                                            16, 256, 0.1, 2, 0, FAKE, 1 << 30, None) == 1
+                                            16, 256, 0.1, 2, FAKE, 1 << 30, None) == 1
 
 
 def _ptrs(*vals):

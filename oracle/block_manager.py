@@ -34,7 +34,10 @@ library's header):
      preceding tokens equal the prompt's, take the one sharing the longest
      run of leading tokens with the prompt's block (ties: the lowest block id).
      A whole 16-token match continues to the next block; anything shorter
-     ends the match.  The matched tokens are served from the cache.
+     ends the match.  The match never takes the prompt's last token: that
+     token's query row is what produces the first output token, so a prompt
+     that is cached whole still prefills its last token.  The matched tokens
+     are served from the cache.
   4. Writing a token at offset o of a block the sequence holds: if another
      sequence holds the block too, copy it first (copy on write) to a newly
      allocated block and write there; if the sequence holds it alone and the
@@ -146,8 +149,11 @@ class BlockManager:
         tokens = list(tokens)
         table, pos = [], 0
         if self.prefix_cache:
-            while pos < len(tokens):
-                b, m = self._lookup(tuple(tokens[:pos]), tokens[pos:pos + BLOCK])
+            # the prompt's last token is never taken from the cache: its query
+            # row yields the first output token, so it must be prefilled
+            limit = len(tokens) - 1
+            while pos < limit:
+                b, m = self._lookup(tuple(tokens[:pos]), tokens[pos:min(pos + BLOCK, limit)])
                 if m == 0:
                     break
                 table.append(b)

@@ -18,19 +18,24 @@
 //   - free blocks form one FIFO queue, initially 0..n-1; allocation takes the
 //     head, a block whose reference count reaches 0 joins the tail, and a freed
 //     sequence releases its blocks last block first;
-//   - a block that holds tokens stays indexed by (hash of all tokens before it,
-//     the tokens it holds) until it is reallocated;
+//   - a block that holds tokens stays indexed by (all tokens before it, the
+//     tokens it holds) until it is reallocated;
 //   - a prompt is matched block by block against the indexed blocks with the
 //     same preceding tokens: the longest run of leading tokens wins (ties: the
 //     lowest block id); a whole-block match continues, a shorter one ends it;
+//     the match never takes the prompt's last token, so at least one query
+//     row is always prefilled (the one that yields the first output token);
 //   - writing at offset o of a block held by another sequence as well copies
 //     it first to a new block (copy on write); a block held alone that has
 //     more than o tokens drops them and is written in place;
 //   - swap out copies every block of a sequence to host blocks (a FIFO queue
 //     of its own) and releases the device blocks; swap in allocates new device
 //     blocks.
-// The index key of a block's position is a 64-bit hash chain over the
-// preceding full blocks; a match also compares the block's own tokens.
+// "All tokens before it" is an exact identity, never a hash: each distinct
+// run of whole blocks from the start of a sequence is interned as a node of a
+// prefix trie (key: the parent node and the 16 token ids, compared in full),
+// and a block is indexed under the node of its preceding tokens.  A node lives
+// while a sequence, an indexed block or a child node refers to it.
 #include <stdint.h>
 #include <string.h>
 
@@ -44,34 +49,40 @@
 namespace {
 
 constexpr int kB = 16;
-constexpr uint64_t kRootKey = 0x6a09e667f3bcc909ull;
+constexpr int32_t kRoot = 0;  // the node of the empty prefix
 
-// Key of the position after a full block: FNV-1a over the block's 16 token
-// ids (4 bytes each, little end first), seeded with the key before it, then a
-// murmur-style finaliser.
-uint64_t chain(uint64_t key, const int32_t* t) {
-  uint64_t h = key ^ 0xcbf29ce484222325ull;
-  for (int i = 0; i < kB; ++i) {
-    uint32_t v = (uint32_t)t[i];
-    for (int k = 0; k < 4; ++k) {
-      h ^= (v >> (8 * k)) & 0xffu;
+// Trie node key: the node of the tokens before a whole block, and the block's
+// 16 token ids.  Equality compares every field; the hash only picks buckets.
+struct NodeKey {
+  int32_t parent;
+  int32_t tok[kB];
+  bool operator==(const NodeKey& o) const {
+    return parent == o.parent && memcmp(tok, o.tok, sizeof(tok)) == 0;
+  }
+};
+struct NodeKeyHash {
+  size_t operator()(const NodeKey& k) const {
+    uint64_t h = 0xcbf29ce484222325ull ^ (uint32_t)k.parent;
+    for (int i = 0; i < kB; ++i) {
+      h ^= (uint32_t)k.tok[i];
       h *= 0x100000001b3ull;
     }
+    return (size_t)(h ^ (h >> 29));
   }
-  h ^= h >> 33;
-  h *= 0xff51afd7ed558ccdull;
-  h ^= h >> 33;
-  h *= 0xc4ceb9fe1a85ec53ull;
-  h ^= h >> 33;
-  return h;
-}
+};
+
+struct Node {
+  NodeKey key;
+  int64_t refs = 0;  // sequences' key lists, indexed blocks and child nodes
+  bool live = false;
+};
 
 struct Block {
   int32_t ref = 0;
   int32_t n_held = 0;
   int32_t held[kB];
   bool indexed = false;
-  uint64_t before = 0;  // key of the tokens before this block, when indexed
+  int32_t before = 0;  // node of the tokens before this block, when indexed
   int32_t prev = -1, next = -1;
   bool in_free = false;
 };
@@ -79,7 +90,7 @@ struct Block {
 struct Seq {
   std::vector<int32_t> table;
   std::vector<int32_t> tokens;
-  std::vector<uint64_t> keys;  // keys[j] = key of tokens[0 .. 16 j)
+  std::vector<int32_t> keys;  // keys[j] = node of tokens[0 .. 16 j), one reference each
   bool swapped = false;
 };
 
@@ -92,7 +103,10 @@ struct pkv_block_manager {
   size_t host_pos = 0;
   int32_t n_host = 0;
   bool prefix_cache = true;
-  std::unordered_map<uint64_t, std::vector<int32_t>> index;
+  std::unordered_map<int32_t, std::vector<int32_t>> index;  // node -> blocks indexed under it
+  std::vector<Node> nodes;
+  std::vector<int32_t> free_nodes;
+  std::unordered_map<NodeKey, int32_t, NodeKeyHash> node_of;
   std::unordered_map<int64_t, Seq> seqs;
   int64_t hit_tokens = 0, query_tokens = 0, hit_requests = 0, requests = 0;
 
@@ -118,6 +132,63 @@ struct pkv_block_manager {
     --n_free;
   }
 
+  // -- prefix trie ------------------------------------------------------------------
+  void init_trie() {
+    nodes.assign(1, Node());
+    nodes[kRoot].live = true;
+    nodes[kRoot].refs = 1;  // the root is never released
+  }
+  static NodeKey key_of(int32_t parent, const int32_t* t) {
+    NodeKey k;
+    k.parent = parent;
+    memcpy(k.tok, t, sizeof(k.tok));
+    return k;
+  }
+  // The node of prefix `parent` followed by the whole block t[0..16), or -1.
+  int32_t find_node(int32_t parent, const int32_t* t) const {
+    auto it = node_of.find(key_of(parent, t));
+    return it == node_of.end() ? -1 : it->second;
+  }
+  // The same node, created if needed, with one reference taken for the caller.
+  int32_t intern(int32_t parent, const int32_t* t) {
+    const NodeKey k = key_of(parent, t);
+    auto it = node_of.find(k);
+    int32_t id;
+    if (it != node_of.end()) {
+      id = it->second;
+    } else {
+      if (!free_nodes.empty()) {
+        id = free_nodes.back();
+        free_nodes.pop_back();
+      } else {
+        id = (int32_t)nodes.size();
+        nodes.emplace_back();
+      }
+      Node& n = nodes[id];
+      n.key = k;
+      n.refs = 0;
+      n.live = true;
+      node_of.emplace(k, id);
+      ++nodes[parent].refs;  // the child's reference
+    }
+    ++nodes[id].refs;
+    return id;
+  }
+  void ref_node(int32_t id) { ++nodes[id].refs; }
+  void unref_node(int32_t id) {
+    while (id != kRoot && --nodes[id].refs == 0) {
+      Node& n = nodes[id];
+      node_of.erase(n.key);
+      n.live = false;
+      free_nodes.push_back(id);
+      id = n.key.parent;  // drop the child's reference to its parent
+    }
+  }
+  void release_keys(Seq& s) {
+    for (int32_t k : s.keys) unref_node(k);
+    s.keys.clear();
+  }
+
   // -- index ----------------------------------------------------------------------
   void unindex(int32_t b) {
     Block& x = blocks[b];
@@ -129,18 +200,20 @@ struct pkv_block_manager {
       if (v.empty()) index.erase(it);
     }
     x.indexed = false;
+    unref_node(x.before);
   }
-  void set_index(int32_t b, uint64_t before) {
+  void set_index(int32_t b, int32_t before) {
     Block& x = blocks[b];
     if (x.indexed && x.before == before) return;
+    ref_node(before);
     unindex(b);
     x.before = before;
     x.indexed = true;
     index[before].push_back(b);
   }
-  // Indexed block with preceding-token key `before` sharing the longest run of
-  // leading tokens with t[0..n); returns the run length (0: none).
-  int lookup(uint64_t before, const int32_t* t, int n, int32_t* best) const {
+  // Indexed block under node `before` sharing the longest run of leading
+  // tokens with t[0..n); returns the run length (0: none).
+  int lookup(int32_t before, const int32_t* t, int n, int32_t* best) const {
     auto it = index.find(before);
     if (it == index.end()) return 0;
     int best_m = 0;
@@ -207,7 +280,7 @@ struct pkv_block_manager {
       x.held[x.n_held++] = t[i];
       s.tokens.push_back(t[i]);
       if (prefix_cache) set_index(b, s.keys[j]);
-      if (o == kB - 1) s.keys.push_back(chain(s.keys[j], &s.tokens[j * kB]));
+      if (o == kB - 1) s.keys.push_back(intern(s.keys[j], &s.tokens[j * kB]));
       slots[i] = (int64_t)b * kB + o;
     }
   }
@@ -234,6 +307,7 @@ pkv_block_manager* pkv_bm_create(int n_blocks, int n_host_blocks, int prefix_cac
     delete m;
     return nullptr;
   }
+  m->init_trie();
   for (int32_t b = 0; b < n_blocks; ++b) m->push_free(b);
   for (int32_t h = 0; h < n_host_blocks; ++h) m->host_free.push_back(h);
   m->n_host = n_host_blocks;
@@ -250,20 +324,22 @@ int pkv_bm_add_sequence(pkv_block_manager* m, int64_t seq_id, const int32_t* tok
     return PKV_ERR_INVALID_ARG;
   if (m->seqs.count(seq_id)) return PKV_ERR_INVALID_ARG;
   Seq s;
-  s.keys.push_back(kRootKey);
   int pos = 0;
   std::vector<int32_t> matched;
   if (m->prefix_cache) {
-    uint64_t key = kRootKey;
-    while (pos < n_tokens) {
+    // The match stops short of the last token: its query row must be prefilled.
+    const int limit = n_tokens - 1;
+    int32_t key = kRoot;
+    while (pos < limit) {
       int32_t b = -1;
-      const int len = std::min(kB, n_tokens - pos);
+      const int len = std::min(kB, limit - pos);
       const int mlen = m->lookup(key, tokens + pos, len, &b);
       if (mlen == 0) break;
       matched.push_back(b);
       pos += mlen;
       if (mlen < kB) break;
-      key = chain(key, tokens + pos - kB);
+      key = m->find_node(key, tokens + pos - kB);
+      if (key < 0) break;  // no block is indexed after this prefix
     }
   }
   int64_t from_free = 0;
@@ -283,9 +359,11 @@ int pkv_bm_add_sequence(pkv_block_manager* m, int64_t seq_id, const int32_t* tok
     m->claim(b);
     s.table.push_back(b);
   }
+  m->ref_node(kRoot);
+  s.keys.push_back(kRoot);
   for (int i = 0; i < pos; ++i) {
     s.tokens.push_back(tokens[i]);
-    if (i % kB == kB - 1) s.keys.push_back(chain(s.keys[i / kB], &s.tokens[i + 1 - kB]));
+    if (i % kB == kB - 1) s.keys.push_back(m->intern(s.keys[i / kB], &s.tokens[i + 1 - kB]));
     slots[i] = -1;
   }
   *n_cow = 0;
@@ -380,6 +458,7 @@ int pkv_bm_fork(pkv_block_manager* m, int64_t parent, int64_t child) {
     return PKV_ERR_INVALID_ARG;
   Seq c = it->second;
   for (int32_t b : c.table) ++m->blocks[b].ref;
+  for (int32_t k : c.keys) m->ref_node(k);
   m->seqs.emplace(child, std::move(c));
   return PKV_OK;
 }
@@ -393,6 +472,7 @@ int pkv_bm_free(pkv_block_manager* m, int64_t seq_id) {
     if (s.swapped) m->host_free.push_back(*b);
     else m->release(*b);
   }
+  m->release_keys(s);
   m->seqs.erase(it);
   return PKV_OK;
 }

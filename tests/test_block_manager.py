@@ -143,6 +143,32 @@ def test_eviction_of_a_cached_free_block():
     assert n == 0
 
 
+@pytest.mark.parametrize("make", [lambda n, h: OBM.BlockManager(n, h),
+                                  lambda n, h: ops.BlockManager(n, h)], ids=["oracle", "library"])
+def test_identical_prompt_resubmitted_prefills_its_last_token(make):
+    """A 40-token prompt fills blocks 0, 1 and 8 slots of 2.  The same prompt
+    again matches blocks 0 and 1 whole and 7 tokens of block 2: its last token
+    (position 39) is written, so block 2, still held by the first request, is
+    copied to block 3 and the token lands at offset 7 (slot 55).  A 32-token
+    prompt resubmitted matches block 0 and 15 tokens of block 1, copies block 1
+    to the next free block and writes position 31 at offset 15.  A 1-token
+    prompt is never cached."""
+    m = make(9, 0)
+    p40 = list(range(100, 140))
+    m.add_sequence(1, p40)
+    n, slots, cow = m.add_sequence(2, p40)
+    assert n == 39 and list(slots[:39]) == [-1] * 39 and slots[39] == 3 * 16 + 7
+    assert [tuple(x) for x in cow] == [(2, 3)]
+    p32 = list(range(200, 232))
+    m.add_sequence(3, p32)                          # blocks 4, 5
+    n, slots, cow = m.add_sequence(4, p32)
+    assert n == 31 and slots[31] == 6 * 16 + 15 and [tuple(x) for x in cow] == [(5, 6)]
+    n, slots, cow = m.add_sequence(5, [7])
+    assert n == 0 and list(slots) == [7 * 16] and len(cow) == 0
+    n, slots, cow = m.add_sequence(6, [7])          # block 7 holds token 7, yet a new block
+    assert n == 0 and list(slots) == [8 * 16] and len(cow) == 0
+
+
 def test_admission_is_all_or_nothing():
     m = OBM.BlockManager(5, n_host_blocks=2)
     m.add_sequence(0, list(range(50)))              # 4 blocks
@@ -187,14 +213,18 @@ def _trace(seed, n_ops, n_blocks, n_host, prefix_cache=True):
     matches happen, forks, appends, frees and swaps."""
     rng = np.random.default_rng(seed)
     systems = [list(rng.integers(0, 50, int(rng.integers(1, 90)))) for _ in range(4)]
-    ops_ = []
+    ops_, prompts = [], []
     for i in range(n_ops):
         r = rng.random()
-        if r < 0.3:
+        if r < 0.06 and prompts:
+            # an identical prompt submitted again (cached whole but its last token)
+            ops_.append(("add", i, list(prompts[int(rng.integers(0, len(prompts)))])))
+        elif r < 0.3:
             sp = systems[int(rng.integers(0, 4))]
             cut = int(rng.integers(0, len(sp) + 1))
             tail = list(rng.integers(0, 6, int(rng.integers(0, 40))))
-            ops_.append(("add", i, sp[:cut] + tail))
+            prompts.append(sp[:cut] + tail)
+            ops_.append(("add", i, prompts[-1]))
         elif r < 0.52:
             ops_.append(("append", int(rng.integers(0, 1 << 30)),
                          list(rng.integers(0, 6, int(rng.integers(1, 6))))))
@@ -277,6 +307,9 @@ def _run(m, lib_m, trace, n_blocks, n_host, check_every=1):
                     assert ro[0] == rl[0] and list(rl[1]) == ro[1], k
                     assert [tuple(p) for p in rl[2]] == ro[2], k
             if ro != "no-blocks":
+                # the last prompt token's query row gives the first output
+                # token, so it is never served from the cache
+                assert ro[0] < len(b) or not b, k
                 live.append(sid)
                 cm.copy(ro[2], cm.dev, cm.dev)
                 cm.write(ro[1], b, 0)
@@ -497,12 +530,38 @@ class ForkWithoutReference(OBM.BlockManager):
                             "swapped": False}
 
 
+class MatchesWholePrompt(OBM.BlockManager):
+    """Serves a prompt cached whole entirely from the cache (no query row left)."""
+    def add_sequence(self, sid, tokens):
+        tokens = list(tokens)
+        if self.prefix_cache and len(tokens) >= 1:
+            table, pos = [], 0
+            while pos < len(tokens):
+                b, m = self._lookup(tuple(tokens[:pos]), tokens[pos:pos + 16])
+                if m == 0:
+                    break
+                table.append(b)
+                pos += m
+                if m < 16:
+                    break
+            if pos == len(tokens) and sid not in self.seqs:
+                for b in table:
+                    self._claim(b)
+                self.seqs[sid] = {"table": table, "tokens": tokens, "swapped": False}
+                self.requests += 1
+                self.query_tokens += pos
+                self.hit_tokens += pos
+                self.hit_requests += 1
+                return pos, [-1] * pos, []
+        return super().add_sequence(sid, tokens)
+
+
 class FreeForgetsQueue(OBM.BlockManager):
     def _release(self, b):
         self.ref[b] -= 1
 
 
 @pytest.mark.parametrize("cls", [NoCopyOnWrite, LookupIgnoresPrefix, LookupWholeBlockOnly,
-                                 ForkWithoutReference, FreeForgetsQueue])
+                                 ForkWithoutReference, FreeForgetsQueue, MatchesWholePrompt])
 def test_planted_mistakes_are_caught(cls):
     assert _caught(cls), cls.__name__

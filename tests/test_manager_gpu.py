@@ -180,6 +180,30 @@ def test_prefix_cache_fork_and_swap_end_to_end():
     assert err <= TOL
 
 
+def test_identical_prompt_resubmitted():
+    """The same prompt submitted twice (a 237-token prompt, and a 224-token one
+    that ends on a block boundary): the second request is served from the
+    cache except its last token, whose query row is prefilled over the shared
+    blocks and a copy on write of the last one, and gives the first output
+    token's attention within tolerance of the oracle; decode steps of both
+    then continue over their own copies."""
+    rng = np.random.default_rng(274104)
+    q_rng = np.random.default_rng(274105)
+    e = Engine()
+    err = 0.0
+    for sid, n in ((1, 237), (3, 224)):
+        prompt = list(rng.integers(0, VOCAB, n))
+        n0, out0, ref0 = e.prefill(sid, prompt, q_rng)
+        assert n0 == 0
+        n1, out1, ref1 = e.prefill(sid + 1, prompt, q_rng)
+        assert n1 == n - 1 and out1.shape[0] == 1
+        err = max(err, max_err(out0, ref0), max_err(out1, ref1))
+    for step in range(3):
+        err = max(err, e.decode_step([1, 2, 3, 4], list(rng.integers(0, VOCAB, 4)), q_rng))
+    print(f"resubmitted prompts max|err| = {err:.3e}")
+    assert err <= TOL
+
+
 def test_cached_prefix_equals_full_recompute():
     """The second request's outputs with its system prompt served from the cache
     equal those of a pool without prefix caching, which prefills all of it."""

@@ -38,7 +38,9 @@ Printed as one JSON line:
   blocks     copy_blocks (copy on write inside a device pool set) and
              swap_blocks (device <-> pinned host pool sets) on decode-shaped
              pools, with a plain torch copy to and from pinned memory beside
-  cpu_baseline  the CPU oracle on the same decode step, on one host core.
+  cpu_baseline  the CPU oracle on the same decode step on the host cores: BLAS
+             on all its threads (value, cores) and pinned to one thread, with
+             the CPU model and the BLAS thread count.
 
 Counter runs and their summaries (written to profiles/):
   python bench.py --profile decode|decode_int8|prefill --steps N    short run for rocprofv3
@@ -365,36 +367,61 @@ def time_manager(steps: int = 200):
             "decode_step_64_seqs_us": round(step_s * 1e6, 1)}
 
 
-def cpu_baseline(w: W.Workload, reps: int):
-    """The oracle (append + decode of the whole step) on the host cores."""
-    import oracle.attention as O
+def _cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w: W.Workload, reps: int):
+    """The oracle (append + decode of the whole step) on the host cores: once
+    with NumPy's BLAS on every thread it starts by default, once pinned to one
+    thread; the median of `reps` steps each.  `value` and `cores` are the
+    all-thread run's."""
+    import oracle.attention as O
+    from threadpoolctl import threadpool_info, threadpool_limits
     q = w.dec_q.to(torch.float64).numpy()
     kc = w.k_cache.to(torch.float64).numpy()
     vc = w.v_cache.to(torch.float64).numpy()
     kn = w.k_new.to(torch.float64).numpy()
     vn = w.v_new.to(torch.float64).numpy()
-    times = []
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    try:
+
+    def run():
+        times = []
         for _ in range(reps):
             t0 = time.perf_counter()
             k2, v2 = O.kv_append(kn, vn, w.slot_mapping.numpy(), kc, vc)
             O.decode(q, k2, v2, w.dec_block_tables.numpy(), w.dec_context_lens.numpy(), w.scale)
             times.append(time.perf_counter() - t0)
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    med = statistics.median(times)
-    return {"value": round(kv_bytes(w) / med / 1e9, 4), "unit": "GB/s", "cores": 1,
+        return statistics.median(times), sum(times)
+
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([int(p.get("num_threads", 1)) for p in blas] or [1])
+    med_all, tot_all = run()
+    with threadpool_limits(limits=1, user_api="blas"):
+        med_1, tot_1 = run()
+    kvb = kv_bytes(w)
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count()
+    return {"value": round(kvb / med_all / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
+            "single_thread_value": round(kvb / med_1 / 1e9, 4),
+            "cpu_model": _cpu_model(),
+            "blas": ",".join(sorted({str(p.get("internal_api", "?")) for p in blas})) or "none",
+            "blas_threads": threads,
+            "usable_cpus": usable,
             "sample": f"{reps} whole decode steps of the same workload (kv_append + decode, "
-                      f"{w.B} sequences, {int(w.dec_context_lens.sum())} context tokens), "
-                      f"median, float64 NumPy with BLAS pinned to 1 thread, "
-                      f"{sum(times):.1f} s total; host {os.cpu_count()} CPUs"}
+                      f"{w.B} sequences, {int(w.dec_context_lens.sum())} context tokens) per "
+                      f"run, median; float64 NumPy with BLAS on {threads} threads "
+                      f"({tot_all:.1f} s), then on 1 thread ({tot_1:.1f} s); "
+                      f"{usable} usable CPUs of {os.cpu_count()}"}
 
 
 # ----------------------------------------------------------------------------
@@ -641,7 +668,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, choices=(3, 4))
     ap.add_argument("--copies", type=int, default=3)
-    ap.add_argument("--cpu-reps", type=int, default=15)
+    ap.add_argument("--cpu-reps", type=int, default=7)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", choices=("decode", "decode_int8", "prefill"))
     ap.add_argument("--summarize", choices=("stats", "traffic", "traffic_int8", "mfma"))

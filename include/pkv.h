@@ -167,6 +167,30 @@ size_t pkv_decode_workspace_bytes_split(int B, int h_q, int h_kv, int d_h, int m
                                         int dtype, int num_splits);
 
 /*
+ * paged_decode_attention_noalloc - paged_decode_attention without a workspace
+ * argument and without any allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The decode workspace is a static device array of
+ * 32 MiB inside the library; each GPU the library runs on holds its own copy
+ * from the first call on that device until the process ends.  The other
+ * arguments, the result and the errors are those of paged_decode_attention,
+ * with these differences:
+ *   - a call whose workspace would exceed 32 MiB returns PKV_ERR_WORKSPACE
+ *     (for example B = 64, h_q = 32, h_kv = 8, d_h = 128, bf16 needs 8.5 MB;
+ *     the size is pkv_decode_workspace_bytes_split(..., num_splits = 0));
+ *   - stream must belong to the current device (else PKV_ERR_INVALID_ARG);
+ *   - every call on one GPU shares that GPU's array: calls that overlap on one
+ *     GPU (two streams, two threads) race and give undefined results.  Calls
+ *     ordered on one stream are safe; nothing in the array needs clearing.
+ */
+int paged_decode_attention_noalloc(void* out, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   int B, int h_q, int h_kv, int d_h, int n_blocks,
+                                   int max_blocks_per_seq, int max_context_len,
+                                   float scale, int dtype, hipStream_t stream);
+
+/*
  * INT8 KV cache.  The cached K and V are quantised dynamically to int8 per
  * token head (LLM Inference Server page, Optional Stretch Challenges, "INT8
  * KV-Cache Quantization") with the symmetric absmax rule of the same page

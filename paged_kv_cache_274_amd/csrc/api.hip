@@ -3,6 +3,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "launch.h"
@@ -270,6 +271,37 @@ size_t pkv_decode_workspace_bytes(int B, int h_q, int d_h, int max_context_len) 
   return pkv::decode_workspace_bound(B, h_q, d_h, max_context_len);
 }
 
+// Device memory of paged_decode_attention_noalloc, for callers that cannot
+// allocate: the decode workspace (partial states, segment descriptors, line
+// length) of one call.  Each GPU holds its own copy until the process ends.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per device
+// (hipGetSymbolAddress with that device current) and kept; nullptr if the
+// runtime cannot provide it.  In host code `scratch` itself only names the
+// symbol: its address is never passed to a kernel.
+static void* static_scratch() {
+  static std::mutex mu;
+  static std::vector<void*> per_device;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if ((size_t)dev >= per_device.size()) per_device.resize((size_t)dev + 1, nullptr);
+  if (!per_device[(size_t)dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    per_device[(size_t)dev] = p;
+  }
+  return per_device[(size_t)dev];
+}
+
 // Both decode entry points: validation, workspace layout and launch.  k_scale
 // and v_scale are used (and required) for the INT8 cache only.
 static int decode_call(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -352,6 +384,36 @@ int paged_decode_attention(void* out, const void* q, const void* k_cache, const 
                                       h_q, h_kv, d_h, n_blocks, max_blocks_per_seq,
                                       max_context_len, scale, dtype, 0, workspace,
                                       workspace_bytes, stream);
+}
+
+int paged_decode_attention_noalloc(void* out, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, int B, int h_q, int h_kv, int d_h,
+                                   int n_blocks, int max_blocks_per_seq, int max_context_len,
+                                   float scale, int dtype, hipStream_t stream) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
+  pkv::KvType kv = dtype == PKV_BF16 ? pkv::KvType::kBF16 : pkv::KvType::kF32;
+  if (!decode_shape_ok(B, h_q, h_kv, max_context_len, 0) || (d_h != 64 && d_h != 128))
+    return decode_call(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, B,
+                       h_q, h_kv, d_h, n_blocks, max_blocks_per_seq, max_context_len, scale, kv,
+                       0, nullptr, 0, stream);  // reports the argument error
+  if (B == 0) return PKV_OK;
+  if (pkv::decode_workspace_bytes(B, h_q, h_kv, d_h, chunks_as_bf16(kv), max_context_len, 0) >
+      kStaticScratchBytes)
+    return PKV_ERR_WORKSPACE;
+  if (stream) {
+    int cur = -1, sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess) {
+      (void)hipGetLastError();
+      return PKV_ERR_HIP;
+    }
+    if (cur != sdev) return PKV_ERR_INVALID_ARG;
+  }
+  void* ws = static_scratch();
+  if (!ws) return PKV_ERR_HIP;
+  return decode_call(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, B,
+                     h_q, h_kv, d_h, n_blocks, max_blocks_per_seq, max_context_len, scale, kv, 0,
+                     ws, kStaticScratchBytes, stream);
 }
 
 int paged_decode_attention_int8(void* out, const void* q, const int8_t* k_cache,

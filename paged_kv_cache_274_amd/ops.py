@@ -25,6 +25,7 @@ EXPORTED = ("kv_append", "paged_decode_attention", "paged_prefill_attention",
             "kv_append_int8", "paged_decode_attention_int8",
             "pkv_decode_workspace_bytes", "pkv_decode_num_splits", "pkv_status_string",
             "paged_decode_attention_split", "pkv_decode_workspace_bytes_split",
+            "paged_decode_attention_noalloc",
             "copy_blocks", "swap_blocks",
             "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_sequence", "pkv_bm_append",
             "pkv_bm_fork", "pkv_bm_free", "pkv_bm_swap_out", "pkv_bm_swap_in",
@@ -81,6 +82,9 @@ def lib() -> ctypes.CDLL:
                                                i32, i32, i32, ctypes.c_float, i32, i32, vp,
                                                ctypes.c_size_t, vp]
     L.paged_decode_attention_split.restype = i32
+    L.paged_decode_attention_noalloc.argtypes = [vp, vp, vp, vp, i32p, i32p, i32, i32, i32, i32,
+                                                 i32, i32, i32, ctypes.c_float, i32, vp]
+    L.paged_decode_attention_noalloc.restype = i32
     L.paged_prefill_attention.argtypes = [vp, vp, i32p, vp, vp, i32p, i32p, i32, i32, i32, i32, i32,
                                           i32, i32, i32, ctypes.c_float, i32, vp]
     L.paged_prefill_attention.restype = i32
@@ -320,6 +324,34 @@ def _decode_launch(out, q, k_cache, v_cache, block_tables, context_lens, B, h_q,
     if int(num_splits) == 0:
         return lib().paged_decode_attention, head + tail
     return lib().paged_decode_attention_split, head + (int(num_splits),) + tail
+
+
+def paged_decode_attention_noalloc(q: torch.Tensor, k_cache: torch.Tensor,
+                                   v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                   context_lens: torch.Tensor, max_context_len: int,
+                                   out: torch.Tensor, scale: Optional[float] = None) -> torch.Tensor:
+    """paged_decode_attention through the entry point that allocates nothing
+    (its workspace is the library's static device array).  out must be given:
+    the binding allocates nothing either."""
+    n_blocks, h_kv, d = _pool_shape(k_cache, v_cache)
+    _need(q.dim() == 3 and q.shape[2] == d and q.dtype == k_cache.dtype, "q must be [B, h_q, d_h]")
+    B, h_q = int(q.shape[0]), int(q.shape[1])
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == B, "block_tables must be int32 [B, max_blocks]")
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (B,),
+          "context_lens must be int32 [B]")
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _dev(q, k_cache, v_cache, block_tables, context_lens, out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rc = lib().paged_decode_attention_noalloc(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), B, h_q, h_kv, d, n_blocks,
+        int(block_tables.shape[1]), int(max_context_len), float(scale), _DTYPE[q.dtype],
+        _stream(q))
+    if rc != 0:
+        raise PkvError("paged_decode_attention_noalloc", rc)
+    return out
 
 
 def bind_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

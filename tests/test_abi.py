@@ -110,6 +110,29 @@ def test_decode_split_validation():
     assert _decode_split(B=0, out=None, q=None) == 0
 
 
+def _noalloc(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, tbl=FAKE, lens=FAKE, B=4, h_q=8, h_kv=2, d=128,
+             nb=64, mb=16, maxc=256, scale=0.1, dt=1)
+    a.update(kw)
+    return ops.lib().paged_decode_attention_noalloc(
+        a["out"], a["q"], a["kc"], a["vc"], a["tbl"], a["lens"], a["B"], a["h_q"], a["h_kv"],
+        a["d"], a["nb"], a["mb"], a["maxc"], a["scale"], a["dt"], None)
+
+
+def test_decode_noalloc_validation():
+    """Argument errors as for paged_decode_attention, and a batch whose
+    workspace exceeds the 32 MiB static array is refused before any HIP call."""
+    assert _noalloc(dt=2) == 1
+    assert _noalloc(h_q=6, h_kv=4) == 1
+    assert _noalloc(d=80) == 2
+    assert _noalloc(B=-1) == 1
+    assert _noalloc(B=0, out=None, q=None) == 0
+    big = 1 << 21          # 2M sequences x 8 KV heads: 128 MiB of segment descriptors alone
+    assert ops.decode_workspace_bytes(big, 8, 8, 128, 16) > 32 << 20
+    assert _noalloc(B=big, h_q=8, h_kv=8, mb=1, maxc=16) == 3
+    assert ops.decode_workspace_bytes(64, 32, 8, 128, 4096) <= 32 << 20
+
+
 @pytest.mark.parametrize("B,h_q,d,maxc", [(64, 32, 128, 4096), (8, 32, 128, 8192), (8, 32, 64, 512),
                                           (60, 14, 64, 2048), (2, 4, 64, 40), (1, 64, 128, 100000),
                                           (3, 1, 64, 0), (300, 8, 128, 17)])

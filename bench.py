@@ -25,6 +25,9 @@ Printed as one JSON line:
              still match the ones it was taken on
   prefill    paged_prefill_attention on the mixed Qwen2.5-0.5B-shaped batch
              (4 prompts x 512 tokens, h_q=14, h_kv=2, d_h=64) in TFLOP/s
+  prefill_long  the same call on 4 causal prompts of 4096 tokens at the
+             Llama-3-8B shape (32/8/128) and the Qwen2.5-0.5B shape (14/2/64),
+             where the kernel is not launch-bound; TFLOP/s against 2.5 PFLOP/s
   verify_decode  the chunked-prefill call with 4 new tokens per sequence of the
              decode batch (a speculative verify step), in KV GB/s
   int8_decode  paged_decode_attention_int8 on the same decode step over an
@@ -74,6 +77,8 @@ COPY_BYTES = 256 << 20           # plain device copy used to calibrate the byte 
 
 SLUG = {3: "llama3-8b-decode-b64", 4: "long-context-prefix-decode-b8",
         5: "qwen2.5-0.5b-prefill-4x512"}
+# long-prompt prefill shapes: (h_q, h_kv, d_h) -> summary name
+LONG_PREFILL = {(32, 8, 128): "llama3-8b-prefill-4x4096", (14, 2, 64): "qwen2.5-0.5b-prefill-4x4096"}
 WORKLOAD = {
     3: "llama3-8b-shaped decode step: B=64, contexts U[128,4096], h_q=32, h_kv=8, d_h=128, "
        "bf16, 16-token blocks, shuffled pool +10% free",
@@ -273,6 +278,26 @@ def time_prefill(r: Resident, iters: int = 50, warmup: int = 5):
     return back_to_back_ms, [a.elapsed_time(b) for a, b in ev]
 
 
+def time_long_prefill(dev: str, iters: int = 10):
+    """prefill_long: back-to-back calls (two HIP events) of 4 x 4096-token
+    causal prefills at each shape of LONG_PREFILL."""
+    res = {}
+    for (h_q, h_kv, d), name in LONG_PREFILL.items():
+        w = W.long_prefill(h_q, h_kv, d)
+        r = Resident(w, dev)
+        r.append(0)
+        ms = time_calls(r.prefill, iters, warmup=3)
+        fl = prefill_flops(w)
+        mf = measured_mfma(name)
+        res[name] = {"flops": fl, "avg_us": round(ms * 1e3, 2),
+                     "tflops": round(fl / (ms / 1e3) / 1e12, 2),
+                     "frac": round(fl / (ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "mfma_util_pct": None if mf is None else mf["mfma_util_pct"]}
+        del r, w
+        torch.cuda.empty_cache()
+    return res
+
+
 def time_copy(dev: str, nbytes: int = 1 << 30, iters: int = 10):
     """Device-to-device copy rate (read + write bytes / time) of a plain 1 GiB copy."""
     src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
@@ -454,8 +479,8 @@ def measured_traffic(k: int):
     return int(f["hbm_bytes_per_call"])
 
 
-def measured_mfma():
-    f = read_summary_fields(summary_path(5, "mfma"))
+def measured_mfma(name: str = SLUG[5]):
+    f = read_summary_fields(os.path.join(PROFILES, f"prefill_{name}_mfma.txt"))
     if f.get("prefill_sources_sha256") != digest(PREFILL_SOURCES):
         return None
     return {"mfma_util_pct": float(f["mfma_util_pct"]),
@@ -532,19 +557,30 @@ def summarize_traffic(k, fetch_csv, write_csv, steps, extra, int8=False):
     return "\n".join(text) + "\n"
 
 
-def summarize_mfma(csv_path, steps):
-    w = W.config(5)
+def _prefill_workload(what: str):
+    """The workload of a prefill profile mode: config 5's prompts, or a long one."""
+    if what == "prefill":
+        return W.config(5), SLUG[5], ("Qwen2.5-0.5B-shaped prefill: 4 prompts x 512 tokens, "
+                                      "h_q=14, h_kv=2, d_h=64")
+    shape = {"prefill_long128": (32, 8, 128), "prefill_long64": (14, 2, 64)}[what]
+    return (W.long_prefill(*shape), LONG_PREFILL[shape],
+            f"4 causal prompts x 4096 tokens, h_q={shape[0]}, h_kv={shape[1]}, d_h={shape[2]}")
+
+
+def summarize_mfma(csv_path, steps, what="prefill"):
+    w, name, desc = _prefill_workload(what)
     ds = _dispatches(csv_path)
     util, n = _avg(ds, "prefill", "MfmaUtil")
     flops, _ = _avg(ds, "prefill", "MfmaFlopsBF16")
     alg = prefill_flops(w)
+    d = "pmc_mfma" if what == "prefill" else f"pmc_mfma_{what}"
     text = [
-        "# MFMA use of one paged_prefill_attention call (Qwen2.5-0.5B-shaped prefill: 4 prompts x",
-        "# 512 tokens, h_q=14, h_kv=2, d_h=64, causal, bf16)",
+        f"# MFMA use of one paged_prefill_attention call ({desc}, causal, bf16)",
         "# command (repository root, on the GPU):",
-        "#   " + CMD_PMC.format(counters="MfmaUtil MfmaFlopsBF16", dir="pmc_mfma", what="prefill",
+        "#   " + CMD_PMC.format(counters="MfmaUtil MfmaFlopsBF16", dir=d, what=what,
                                 steps=steps, args=""),
-        f"#   python bench.py --summarize mfma --steps {steps} gpurun_out/pmc_mfma/run_counter_collection.csv",
+        f"#   python bench.py --summarize mfma --profile {what} --steps {steps} "
+        f"gpurun_out/{d}/run_counter_collection.csv",
         "# MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), percent, per dispatch;",
         "# MfmaFlopsBF16 = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, per dispatch.",
         f"# {n} prefill dispatches; algorithmic flops per call {alg} (causal pairs incl. diagonal);",
@@ -653,7 +689,8 @@ def profile_run(what: str, k: int, steps: int, dev: str):
         for i in range(steps):
             r8.decode(i)
     else:
-        r = Resident(W.config(5), dev)
+        w, _, _ = _prefill_workload(what)
+        r = Resident(w, dev)
         r.append(0)
         for i in range(steps):
             r.prefill(i)
@@ -670,7 +707,8 @@ def main(argv=None):
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--cpu-reps", type=int, default=7)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile", choices=("decode", "decode_int8", "prefill"))
+    ap.add_argument("--profile", choices=("decode", "decode_int8", "prefill", "prefill_long128",
+                                          "prefill_long64"))
     ap.add_argument("--summarize", choices=("stats", "traffic", "traffic_int8", "mfma"))
     ap.add_argument("inputs", nargs="*")
     args = ap.parse_args(argv)
@@ -684,8 +722,9 @@ def main(argv=None):
                                      int8=int8)
             path = summary_path(args.config, "int8_hbm_traffic" if int8 else "hbm_traffic")
         elif args.summarize == "mfma":
-            text = summarize_mfma(args.inputs[0], args.steps)
-            path = summary_path(5, "mfma")
+            what = args.profile or "prefill"
+            text = summarize_mfma(args.inputs[0], args.steps, what)
+            path = os.path.join(PROFILES, f"prefill_{_prefill_workload(what)[1]}_mfma.txt")
         else:
             text = summarize_stats(args.inputs[0], args.inputs[1], extra)
             path = summary_path(args.config, "kernel_stats")
@@ -776,6 +815,7 @@ def main(argv=None):
     del r5
     torch.cuda.empty_cache()
 
+    prefill_long = time_long_prefill(dev)
     copy_gbs = time_copy(dev)
     blocks = time_blocks(dev)
     blocks["manager"] = time_manager()
@@ -875,6 +915,7 @@ def main(argv=None):
             "frac": round(pf_tflops / BF16_MFMA_PEAK_TFLOPS, 5),
             "mfma_util_pct": None if mfma is None else mfma["mfma_util_pct"],
         },
+        "prefill_long": prefill_long,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wk, args.cpu_reps)

@@ -287,3 +287,13 @@ def int8_pools(w: Workload, seed: int, poison: bool = False) -> Int8Pools:
         vs[unused] = np.nan
     return Int8Pools(torch.from_numpy(kq), torch.from_numpy(vq), torch.from_numpy(ks),
                      torch.from_numpy(vs))
+
+
+def long_prefill(h_q: int, h_kv: int, d: int, prompts: int = 4, length: int = 4096,
+                 seed: int = 274020) -> Workload:
+    """Long causal prompts prefilled whole (``prompts`` x ``length`` tokens, the
+    K/V of every token already appended), for measuring the prefill kernel away
+    from its launch ramp.  Pool = used blocks + 10% free, shuffled."""
+    return build(f"prefill-{prompts}x{length}-{h_q}/{h_kv}/{d}", np.random.default_rng(seed),
+                 dtype="bf16", h_q=h_q, h_kv=h_kv, d=d,
+                 prefill=[(length, length)] * prompts, free_frac=0.10)

@@ -15,7 +15,8 @@ with wall clock between two synchronisations.
 Printed as one JSON line:
   value      KV bytes attended per second (GB/s), whole step (append + decode)
   roofline   the decode call (its two kernels; HIP events on the launch stream
-             around K back-to-back calls after the timed steps; in_step_* from
+             around each of 5 batches of max(K, 20) back-to-back calls after
+             the timed steps and 50 warm-up calls, median batch; in_step_* from
              events around each call of K more steps) against the 8 TB/s HBM
              peak; algorithmic bytes per
              call = sum_b L_b * 2 * h_kv * d_h * 2 B (the KV-cache footprint
@@ -201,19 +202,24 @@ def time_step_parts(r: Resident, steps: int):
     return app_ms, dec_ms
 
 
-def time_decode_calls(r: Resident, iters: int, warmup: int = 3):
-    """Average duration of one decode call, from two HIP events around `iters`
-    back-to-back calls on the launch stream (no per-call event overhead)."""
+def time_decode_calls(r: Resident, iters: int, warmup: int = 50, batches: int = 5):
+    """Duration of one decode call: two HIP events on the launch stream around
+    each of `batches` batches of `iters` back-to-back calls (no per-call event
+    overhead), after `warmup` calls (the first few dozen calls after the
+    pools are set up run about 5% slower).  Returns (median, [per-batch ms])."""
     for i in range(warmup):
         r.decode(i)
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(iters):
-        r.decode(i)
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / iters
+    per = []
+    for _ in range(batches):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(iters):
+            r.decode(i)
+        b.record()
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) / iters)
+    return statistics.median(per), per
 
 
 class ResidentInt8:
@@ -752,7 +758,8 @@ def main(argv=None):
     wall = time_steps(rk, args.steps, args.warmup)
     kvb = kv_bytes(wk)
     value = kvb * args.steps / wall / 1e9
-    dec_avg_s = time_decode_calls(rk, args.steps) / 1e3
+    dec_med_ms, dec_batches_ms = time_decode_calls(rk, max(args.steps, 20))
+    dec_avg_s = dec_med_ms / 1e3
     app_ms, dec_ms = time_step_parts(rk, args.steps)
     achieved = kvb / dec_avg_s / 1e9
     app_bytes = 2 * wk.T * wk.h_kv * wk.d * wk.elem_bytes * 2 + wk.T * 8
@@ -784,7 +791,7 @@ def main(argv=None):
     if args.config == 3:
         w4 = W.config(4)
         r4 = Resident(w4, dev, copies=args.copies)
-        l_ms = time_calls(r4.decode, args.steps, warmup=5)
+        l_ms, l_batches = time_decode_calls(r4, max(args.steps, 20))
         kvb4 = kv_bytes(w4)
         uniq4 = w4.n_blocks * 16 * 2 * w4.h_kv * w4.d * w4.elem_bytes
         del r4
@@ -853,6 +860,7 @@ def main(argv=None):
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "avg_us": round(dec_avg_s * 1e6, 2),
+            "batches_us": [round(x * 1e3, 2) for x in dec_batches_ms],
             "in_step_avg_us": round(statistics.mean(dec_ms) * 1e3, 2),
             "in_step_median_us": round(pct(dec_ms, 50) * 1e3, 2),
             "in_step_p10_us": round(pct(dec_ms, 10) * 1e3, 2),
@@ -889,6 +897,7 @@ def main(argv=None):
             "kv_bytes": kvb4,
             "unique_kv_bytes": uniq4,
             "avg_us": round(l_ms * 1e3, 2),
+            "batches_us": [round(x * 1e3, 2) for x in l_batches],
             "GBps": round(kvb4 / (l_ms / 1e3) / 1e9, 1),
             "unique_GBps": round(uniq4 / (l_ms / 1e3) / 1e9, 1),
             "frac": round(kvb4 / (l_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -176,8 +176,9 @@ size_t pkv_decode_workspace_bytes_split(int B, int h_q, int h_kv, int d_h, int m
  * arguments, the result and the errors are those of paged_decode_attention,
  * with these differences:
  *   - a call whose workspace would exceed 32 MiB returns PKV_ERR_WORKSPACE
- *     (for example B = 64, h_q = 32, h_kv = 8, d_h = 128, bf16 needs 8.5 MB;
- *     the size is pkv_decode_workspace_bytes_split(..., num_splits = 0));
+ *     (the size is pkv_decode_workspace_bytes_split(..., num_splits) at the
+ *     automatic split count, pkv_decode_num_splits(..., 0); for example
+ *     B = 64, h_q = 32, h_kv = 8, d_h = 128, bf16 at 2048 splits needs 8.5 MB);
  *   - stream must belong to the current device (else PKV_ERR_INVALID_ARG);
  *   - every call on one GPU shares that GPU's array: calls that overlap on one
  *     GPU (two streams, two threads) race and give undefined results.  Calls

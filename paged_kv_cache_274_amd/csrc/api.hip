@@ -398,8 +398,12 @@ int paged_decode_attention_noalloc(void* out, const void* q, const void* k_cache
                        h_q, h_kv, d_h, n_blocks, max_blocks_per_seq, max_context_len, scale, kv,
                        0, nullptr, 0, stream);  // reports the argument error
   if (B == 0) return PKV_OK;
-  if (pkv::decode_workspace_bytes(B, h_q, h_kv, d_h, chunks_as_bf16(kv), max_context_len, 0) >
-      kStaticScratchBytes)
+  // The automatic split, stated explicitly: the same launch as
+  // paged_decode_attention, with the workspace sized for the count in use
+  // rather than for the largest automatic count.
+  const int splits = auto_splits(B, h_q, h_kv, d_h, max_context_len, kv);
+  if (pkv::decode_workspace_bytes(B, h_q, h_kv, d_h, chunks_as_bf16(kv), max_context_len,
+                                  splits) > kStaticScratchBytes)
     return PKV_ERR_WORKSPACE;
   if (stream) {
     int cur = -1, sdev = -1;
@@ -412,8 +416,8 @@ int paged_decode_attention_noalloc(void* out, const void* q, const void* k_cache
   void* ws = static_scratch();
   if (!ws) return PKV_ERR_HIP;
   return decode_call(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, B,
-                     h_q, h_kv, d_h, n_blocks, max_blocks_per_seq, max_context_len, scale, kv, 0,
-                     ws, kStaticScratchBytes, stream);
+                     h_q, h_kv, d_h, n_blocks, max_blocks_per_seq, max_context_len, scale, kv,
+                     splits, ws, kStaticScratchBytes, stream);
 }
 
 int paged_decode_attention_int8(void* out, const void* q, const int8_t* k_cache,

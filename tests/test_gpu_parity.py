@@ -132,6 +132,34 @@ def test_decode_split_invariance(splits):
     check_decode(w, res, kc_ref, vc_ref)
 
 
+def test_decode_workspace_reused_across_shapes():
+    """One workspace serves calls of different shapes in turn, whatever an
+    earlier call left in it: results are bit-identical to calls on fresh
+    workspaces."""
+    shapes = [("bf16", 32, 8, 128, [int(x) for x in np.random.default_rng(3).integers(1, 3000, 40)]),
+              ("bf16", 14, 2, 64, [int(x) for x in np.random.default_rng(4).integers(1, 2000, 60)]),
+              ("f32", 8, 2, 64, [5, 700, 1200])]
+    runs = []
+    for i, (dt, h_q, h_kv, d, lens) in enumerate(shapes):
+        w = W.build("reuse", np.random.default_rng(60 + i), dtype=dt, h_q=h_q, h_kv=h_kv, d=d,
+                    decode_lens=lens, free_frac=0.1, poison=True)
+        kc, vc = w.k_cache.to(DEV), w.v_cache.to(DEV)
+        ops.kv_append(w.k_new.to(DEV), w.v_new.to(DEV), w.slot_mapping.to(DEV), kc, vc)
+        runs.append((w, kc, vc, w.dec_q.to(DEV), w.dec_block_tables.to(DEV),
+                     w.dec_context_lens.to(DEV)))
+    size = max(ops.decode_workspace_bytes(w.B, w.h_q, w.h_kv, w.d, w.dec_max_context_len, w.dtype)
+               for w, *_ in runs)
+    shared = torch.full((size,), 0xA5, dtype=torch.uint8, device=DEV)
+    for rep in range(2):
+        for w, kc, vc, q, tbl, lens in runs:
+            fresh = ops.paged_decode_attention(q, kc, vc, tbl, lens, w.dec_max_context_len,
+                                               scale=w.scale)
+            again = ops.paged_decode_attention(q, kc, vc, tbl, lens, w.dec_max_context_len,
+                                               scale=w.scale, workspace=shared)
+            torch.cuda.synchronize()
+            assert torch.equal(bits(fresh.cpu()), bits(again.cpu())), (w.h_q, w.d, rep)
+
+
 CURSOR_MIXES = [
     # name, lens, h_q, h_kv, d
     ("many short", [int(x) for x in np.random.default_rng(41).integers(1, 40, size=300)], 8, 2, 64),
@@ -376,7 +404,7 @@ def test_bound_calls_match_the_checked_calls():
     q, tbl, lens = w.dec_q.to(dev), w.dec_block_tables.to(dev), w.dec_context_lens.to(dev)
     ops.kv_append(k_new, v_new, slots, *pools[0])
     ops.bind_kv_append(k_new, v_new, slots, *pools[1])()
-    ws = torch.empty(ops.decode_workspace_bytes(w.B, w.h_q, w.h_kv, w.d, w.dec_max_context_len),
+    ws = torch.zeros(ops.decode_workspace_bytes(w.B, w.h_q, w.h_kv, w.d, w.dec_max_context_len),
                      dtype=torch.uint8, device=dev)
     out_a = ops.paged_decode_attention(q, *pools[0], tbl, lens, w.dec_max_context_len,
                                        scale=w.scale)

@@ -26,8 +26,10 @@ What it computes, in the pages' order and notation:
   like the bf16 pools.
 
 * Attention over an INT8 cache is attention over the dequantised values
-  x_hat = s * x_q (exact in float64), i.e. ``attention.decode`` applied to the
-  dequantised pools.
+  x_hat = s * x_q (exact in float64): ``attention.decode`` and
+  ``attention.prefill`` (causal chunked prefill, the prompt processed in
+  parallel over the cache, LLM Inference Server page, Stage 1 prefill/decode
+  task) applied to the dequantised pools.
 """
 from __future__ import annotations
 
@@ -91,3 +93,10 @@ def decode_int8(q, k_codes, v_codes, k_scales, v_scales, block_tables, context_l
     """Decode attention over the dequantised cache (float64)."""
     return A.decode(q, dequantize(k_codes, k_scales), dequantize(v_codes, v_scales), block_tables,
                     context_lens, scale)
+
+
+def prefill_int8(q, cu_seqlens, k_codes, v_codes, k_scales, v_scales, block_tables,
+                 context_lens, scale: float) -> np.ndarray:
+    """Causal chunked prefill over the dequantised cache (float64)."""
+    return A.prefill(q, cu_seqlens, dequantize(k_codes, k_scales), dequantize(v_codes, v_scales),
+                     block_tables, context_lens, scale)

@@ -219,6 +219,88 @@ def test_decode_int8_block_permutation():
     assert np.array_equal(a, b)
 
 
+def _integer_cache(rng, nb, h_kv, d):
+    """Integer rows with max |x| = 127: they quantise to themselves with s = 1."""
+    kf = rng.integers(-126, 127, size=(nb, h_kv, 16, d)).astype(np.float32)
+    vf = rng.integers(-126, 127, size=(nb, h_kv, 16, d)).astype(np.float32)
+    kf[..., 2] = -127.0
+    vf[..., 0] = 127.0
+    kq = np.zeros(kf.shape, np.int8)
+    vq = np.zeros(vf.shape, np.int8)
+    ks = np.zeros(kf.shape[:3], np.float32)
+    vs = np.zeros(vf.shape[:3], np.float32)
+    for idx in np.ndindex(*kf.shape[:3]):
+        kq[idx], ks[idx] = Q.quantize_row(kf[idx])
+        vq[idx], vs[idx] = Q.quantize_row(vf[idx])
+    assert np.all(ks == 1) and np.all(vs == 1)
+    return kf, vf, kq, vq, ks, vs
+
+
+def test_exactly_representable_cache_prefills_like_the_plain_cache():
+    """Chunked prefill (a 20-token chunk at the end of a 45-token context, a
+    whole 30-token prompt) over an integer cache with s = 1 equals the plain
+    prefill of the same values, bit for bit."""
+    rng = np.random.default_rng(13)
+    kf, vf, kq, vq, ks, vs = _integer_cache(rng, 7, 2, 16)
+    q = rng.standard_normal((50, 6, 16)) * 0.05
+    cu = np.array([0, 20, 50], np.int32)
+    tables = np.array([[4, 0, 6], [1, 3, 5]], dtype=np.int32)
+    lens = np.array([45, 30])
+    assert np.array_equal(Q.prefill_int8(q, cu, kq, vq, ks, vs, tables, lens, 0.25),
+                          A.prefill(q, cu, kf, vf, tables, lens, 0.25))
+
+
+def _brute_prefill_int8(q, cu, kq, vq, ks, vs, tables, lens, scale):
+    """Pure-Python prefill over s * x_q, element by element."""
+    kd = [[[[float(ks[b, h, o]) * int(kq[b, h, o, c]) for c in range(kq.shape[3])]
+            for o in range(16)] for h in range(kq.shape[1])] for b in range(kq.shape[0])]
+    vd = [[[[float(vs[b, h, o]) * int(vq[b, h, o, c]) for c in range(vq.shape[3])]
+            for o in range(16)] for h in range(vq.shape[1])] for b in range(vq.shape[0])]
+    return pins.brute_prefill(q, cu, np.array(kd), np.array(vd), tables, lens, scale)
+
+
+def _check_prefill_int8_brute(prefill_int8):
+    rng = np.random.default_rng(14)
+    kq, vq, ks, vs = _random_int8_cache(rng, 7, 2, 8)
+    q = rng.standard_normal((27, 4, 8))
+    cu = np.array([0, 17, 20, 27], np.int32)
+    tables = np.array([[6, 0, 3], [2, 5, 1], [4, 0, 0]], dtype=np.int32)
+    lens = np.array([37, 20, 7])
+    got = prefill_int8(q, cu, kq, vq, ks, vs, tables, lens, 0.3)
+    ref = _brute_prefill_int8(q, cu, kq, vq, ks, vs, tables, lens, 0.3)
+    assert np.abs(got - ref).max() <= 1e-12
+
+
+def test_prefill_int8_matches_brute_force():
+    _check_prefill_int8_brute(Q.prefill_int8)
+
+
+def test_prefill_int8_last_row_is_decode():
+    """The last query row of a prefill is the decode of that token over the
+    same cache (cached equals recomputed, LLM Inference Server page, Stage 1)."""
+    rng = np.random.default_rng(15)
+    kq, vq, ks, vs = _random_int8_cache(rng, 6, 2, 8)
+    q = rng.standard_normal((9, 4, 8))
+    tables = np.array([[5, 2, 0]], dtype=np.int32)
+    lens = np.array([41])
+    pre = Q.prefill_int8(q, np.array([0, 9], np.int32), kq, vq, ks, vs, tables, lens, 0.2)
+    dec = Q.decode_int8(q[-1:], kq, vq, ks, vs, tables, lens, 0.2)
+    assert np.abs(pre[-1] - dec[0]).max() <= 1e-13
+
+
+def test_mutation_scale_on_the_wrong_axis_is_caught(monkeypatch):
+    """A dequantisation that takes the scale along the channel axis (scale of
+    slot c % 16 for channel c) instead of one scale per token row fails the
+    brute-force pin."""
+    def wrong_axis(codes, scales):
+        c = np.asarray(codes, dtype=np.float64)
+        s = np.asarray(scales, dtype=np.float64)
+        ch = np.arange(c.shape[-1]) % 16
+        return c * s[..., ch][..., None, :]
+    monkeypatch.setattr(Q, "dequantize", wrong_axis)
+    assert _fails(_check_prefill_int8_brute, Q.prefill_int8)
+
+
 def test_kv_append_int8_writes_only_the_named_slots():
     rng = np.random.default_rng(6)
     kq, vq, ks, vs = _random_int8_cache(rng, 4, 2, 8)

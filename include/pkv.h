@@ -272,6 +272,27 @@ int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_
                             hipStream_t stream);
 
 /*
+ * paged_prefill_attention_int8 - paged_prefill_attention over an INT8 cache:
+ * the same causal chunked prefill with K and V replaced by x_hat = s * x_q,
+ * for chunked prefill, prefill after a prefix-cache hit and multi-token
+ * decode over a cache quantised as above.  q and out are bf16 [T_q, h_q, d_h];
+ * k_cache, v_cache, k_scale, v_scale as for paged_decode_attention_int8
+ * (scale pools 16-byte aligned); the other arguments as for
+ * paged_prefill_attention.  The codes are widened exactly to bf16 for the
+ * matrix products; the K scale multiplies each score and the V scale each
+ * softmax weight, which is rounded to bf16 as in the bf16 prefill;
+ * accumulation is in fp32.  Slots past a sequence's context are never used,
+ * whatever they hold.
+ */
+int paged_prefill_attention_int8(void* out, const void* q, const int32_t* cu_seqlens_q,
+                                 const int8_t* k_cache, const int8_t* v_cache,
+                                 const float* k_scale, const float* v_scale,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int S, int T_q, int max_q_len, int h_q, int h_kv, int d_h,
+                                 int n_blocks, int max_blocks_per_seq, float scale,
+                                 hipStream_t stream);
+
+/*
  * Block copies between KV pools.
  *
  * A pool set is the pools of one layer that share one block numbering: the K

@@ -465,6 +465,7 @@ int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_
     if (rc != PKV_OK) return rc;
   }
   pkv::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
   a.out = out;
   a.q = q;
   a.cu_seqlens_q = cu_seqlens_q;
@@ -482,6 +483,62 @@ int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.scale_log2 = scale * kLog2e;
   return from_hip(pkv::launch_prefill_bf16(a, d_h, s));
+}
+
+int paged_prefill_attention_int8(void* out, const void* q, const int32_t* cu_seqlens_q,
+                                 const int8_t* k_cache, const int8_t* v_cache,
+                                 const float* k_scale, const float* v_scale,
+                                 const int32_t* block_tables, const int32_t* context_lens, int S,
+                                 int T_q, int max_q_len, int h_q, int h_kv, int d_h, int n_blocks,
+                                 int max_blocks_per_seq, float scale, hipStream_t stream) {
+  if (S < 0 || T_q < 0 || max_q_len < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0 ||
+      n_blocks <= 0 || max_blocks_per_seq <= 0 || !isfinite(scale))
+    return PKV_ERR_INVALID_ARG;
+  if (d_h != 64 && d_h != 128) return PKV_ERR_UNSUPPORTED;
+  if (S == 0 || T_q == 0 || max_q_len == 0) return PKV_OK;
+  if (S > 65535 || h_kv > 65535) return PKV_ERR_UNSUPPORTED;
+  if (!out || !q || !cu_seqlens_q || !k_cache || !v_cache || !k_scale || !v_scale ||
+      !block_tables || !context_lens)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(k_scale) || !aligned16(v_scale) || ((uintptr_t)block_tables & 3u) ||
+      ((uintptr_t)context_lens & 3u) || ((uintptr_t)cu_seqlens_q & 3u))
+    return PKV_ERR_INVALID_ARG;
+  hipStream_t s = stream;
+  if (debug_checks()) {
+    std::vector<int32_t> cu, l;
+    if (!copy_to_host(cu, cu_seqlens_q, (size_t)S + 1, s)) return PKV_ERR_HIP;
+    if (!copy_to_host(l, context_lens, (size_t)S, s)) return PKV_ERR_HIP;
+    if (cu[0] != 0 || cu[S] != T_q) return PKV_ERR_INVALID_ARG;
+    for (int i = 0; i < S; ++i) {
+      const int n = cu[i + 1] - cu[i];
+      if (n < 0 || n > max_q_len || n > l[i]) return PKV_ERR_INVALID_ARG;
+    }
+    const int rc = debug_check_tables(block_tables, context_lens, S, max_blocks_per_seq,
+                                      max_blocks_per_seq * 16, n_blocks, s);
+    if (rc != PKV_OK) return rc;
+  }
+  pkv::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.out = out;
+  a.q = q;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.S = S;
+  a.T_q = T_q;
+  a.max_q_len = max_q_len;
+  a.h_q = h_q;
+  a.h_kv = h_kv;
+  a.g = h_q / h_kv;
+  a.n_blocks = n_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale_log2 = scale * kLog2e;
+  return from_hip(pkv::launch_prefill_i8(a, d_h, s));
 }
 
 int copy_blocks(void* const* pools, const int64_t* block_bytes, int n_pools, int n_blocks,

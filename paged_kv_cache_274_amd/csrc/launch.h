@@ -145,12 +145,16 @@ struct PrefillArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const float* k_scale;  // INT8 cache only: [n_blocks, h_kv, 16]
+  const float* v_scale;
   int S, T_q, max_q_len, h_q, h_kv, g, n_blocks, max_blocks_per_seq;
   float scale_log2;
   int longest_first;  // set by the launcher: sequence planes taken longest context first
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d_h, hipStream_t stream);
+// Prefill over an INT8 cache (codes and float32 scales), bf16 queries and output.
+hipError_t launch_prefill_i8(const PrefillArgs& a, int d_h, hipStream_t stream);
 
 // Block copies between pool sets: up to kMaxCopyPools pools (K, V, and for the
 // INT8 cache their scales) share one block mapping.  src/dst are device

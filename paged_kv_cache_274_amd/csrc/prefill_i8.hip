@@ -1,0 +1,344 @@
+// Causal chunked prefill over an INT8 KV cache with bf16 matrix cores (gfx950).
+//
+// The cache holds x_hat = s * x_q: int8 codes with one float32 scale per token
+// head row (LLM Inference Server page, Optional Stretch Challenges, "INT8
+// KV-Cache Quantization"), and the new prompt tokens are processed in parallel
+// over it with causal masking (Stage 1 prefill/decode task of the same page;
+// Attention Kernel box of the pipeline figure, From Scratch page).
+//
+// Design: the bf16 prefill's tiling and matrix products (prefill.hip: GQA rows
+// packed, 128 rows per workgroup of 4 waves, 64-key tiles, S^T = K Q^T and
+// O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, lazy-rescale online softmax),
+// with the cache read as codes:
+//  * the codes and scales of a tile (half the bytes of a bf16 tile) are copied
+//    straight from HBM into one of three LDS staging buffers, two tiles ahead;
+//  * all 256 threads widen the tile's codes exactly to bf16 (|c| <= 127 needs
+//    8 significant bits) into the swizzled bf16 tile layout the matrix reads
+//    use, once per workgroup, and write the tile's scales with the keys past
+//    the context set to 0 (their slots may hold anything) and the K scales
+//    multiplied by |scale| * log2(e);
+//  * the K scale multiplies each score S^T (one key per accumulator element);
+//    the V scale multiplies each softmax weight before it is rounded to bf16
+//    for the P^T operand (the normaliser sums the unscaled weights), so
+//    attention is over x_hat exactly up to the bf16 rounding of the weights,
+//    as in the bf16 and INT8 decodes.
+#include "prefill_common.h"
+
+namespace pkv {
+
+namespace {
+
+// Codes c0..c3 of a dword as two bf16 pairs, exactly: an int8 converts to
+// float32 without rounding, and with at most 8 significant bits its float32
+// pattern ends in 16 zero bits.
+__device__ __forceinline__ void widen4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const float f0 = (float)(int)(int8_t)(w & 0xff);
+  const float f1 = (float)(int)(int8_t)((w >> 8) & 0xff);
+  const float f2 = (float)(int)(int8_t)((w >> 16) & 0xff);
+  const float f3 = (float)(int)(int8_t)(w >> 24);
+  lo = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+}
+
+// A tile of codes as staged: K codes, V codes (64 rows of D bytes each), then
+// the raw K and V scales of its four blocks.
+template <int D>
+struct I8Stage {
+  static constexpr int kCodeMat = kPfTile * D;
+  static constexpr int kBytes = 2 * kCodeMat + 2 * kPfTile * 4;
+  static constexpr int kCopiesPerBlock = kBlock * D / 1024;  // 1 KiB copies per block of codes
+};
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_i8_kernel(PrefillArgs a) {
+  using Tl = PfTile<D>;
+  using St = I8Stage<D>;
+  // LDS: three staging buffers (codes of K and V, raw K and V scales), one
+  // bf16 tile (K then V), and the tile's sanitised scales (K, then V).
+  __shared__ __attribute__((aligned(16))) unsigned char lds[3 * St::kBytes + 2 * Tl::kMatBytes +
+                                                            2 * kPfTile * 4];
+  unsigned char* const tile = lds + 3 * St::kBytes;
+  float* const ksc = reinterpret_cast<float*>(tile + 2 * Tl::kMatBytes);
+  float* const vsc = ksc + kPfTile;
+  constexpr int NC = D / 16;
+  constexpr int NT = D / 32;
+  // copies per wave per tile: its block's K and V codes, plus one for the scales
+  constexpr int kCopies = 2 * St::kCopiesPerBlock + 1;
+
+  const int bx = gridDim.x - 1 - blockIdx.x;
+  const int s = a.longest_first ? longest_first_sequence(a, blockIdx.z) : (int)blockIdx.z;
+  const int kvh = blockIdx.y;
+  const int g = a.g;
+  const int q0 = a.cu_seqlens_q[s];
+  const int n = a.cu_seqlens_q[s + 1] - q0;
+  int L = a.context_lens[s];
+  L = max(0, min(L, a.max_blocks_per_seq * kBlock));
+  const int rows = n * g;
+  const int r0 = bx * kPfRows;
+  if (n <= 0 || n > L || r0 >= rows || q0 < 0 || q0 + n > a.T_q) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int first = L - n;
+
+  const int r = r0 + wave * 32 + col;
+  const bool row_ok = r < rows;
+  const int tok = row_ok ? r / g : n - 1;
+  const int hh = row_ok ? r - (r / g) * g : 0;
+  const int pos = first + tok;
+  const int wave_r0 = r0 + wave * 32;
+  const bool wave_live = wave_r0 < rows;
+  const int wave_pos_lo = first + wave_r0 / g;
+  const int wave_pos_hi = first + (min(wave_r0 + 31, rows - 1)) / g;
+  const int wg_pos_hi = first + (min(r0 + kPfRows - 1, rows - 1)) / g;
+  const int n_tiles = __builtin_amdgcn_readfirstlane(wg_pos_hi / kPfTile + 1);
+  const int Lu = __builtin_amdgcn_readfirstlane(L);
+
+  const float csc = fabsf(a.scale_log2);
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  f32x16_t o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+  float m = kPfNegInf;
+  float lsum = 0.f;
+
+  const unsigned char* kc = reinterpret_cast<const unsigned char*>(a.k_cache);
+  const unsigned char* vc = reinterpret_cast<const unsigned char*>(a.v_cache);
+  const unsigned char* ks = reinterpret_cast<const unsigned char*>(a.k_scale);
+  const unsigned char* vs = reinterpret_cast<const unsigned char*>(a.v_scale);
+  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  auto stage = [&](int kt) { return lds + (kt % 3) * St::kBytes; };
+
+  // Copies block (4 * kt + wave) of tile kt into its staging buffer: the K and
+  // V codes of that block (rows 16 * wave ..), and its 16 K and 16 V scales
+  // (lanes 0-3 and 4-7 of one more copy) into the scale area (wave w's block
+  // at floats 32 w .. 32 w + 31: K then V).
+  auto issue_tile = [&](int kt) {
+    const int bi = min(kt * (kPfTile / kBlock) + wave, a.max_blocks_per_seq - 1);
+    int blk = constant_view(trow)[bi];
+    blk = (blk >= 0 && blk < a.n_blocks) ? blk : 0;
+    const size_t bh = (size_t)blk * a.h_kv + kvh;
+    unsigned char* st = stage(kt);
+#pragma unroll
+    for (int i = 0; i < St::kCopiesPerBlock; ++i) {
+      const size_t src = bh * (kBlock * D) + (size_t)i * 1024 + lane * 16;
+      const int dst = wave * kBlock * D + i * 1024;
+      copy_to_lds(kc + src, st + dst);
+      copy_to_lds(vc + src, st + St::kCodeMat + dst);
+    }
+    if (lane < 8) {
+      const unsigned char* src = (lane < 4 ? ks : vs) + bh * (kBlock * 4) + (lane & 3) * 16;
+      copy_to_lds(src, st + 2 * St::kCodeMat + wave * 128);
+    }
+  };
+
+  // Widens tile kt's codes (staged) into the bf16 tile and writes its
+  // sanitised scales (all threads).  Rows past the context: V zero, both
+  // scales zero.
+  auto convert_tile = [&](int kt) {
+    const unsigned char* st = stage(kt);
+    const int valid = Lu - kt * kPfTile;  // rows of this tile inside the context
+    constexpr int kUnits = 2 * kPfTile * Tl::kChunks;  // 8-code units of K and V
+#pragma unroll
+    for (int u0 = 0; u0 < kUnits; u0 += 256) {
+      const int u = u0 + tid;
+      const int isv = u >= kPfTile * Tl::kChunks;
+      const int uu = isv ? u - kPfTile * Tl::kChunks : u;
+      const int row = uu / Tl::kChunks;
+      const int ch = uu - row * Tl::kChunks;
+      const uint2 w = *reinterpret_cast<const uint2*>(st + isv * St::kCodeMat + row * D + ch * 8);
+      uint4 x;
+      widen4(w.x, x.x, x.y);
+      widen4(w.y, x.z, x.w);
+      if (isv && row >= valid) x = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(tile + isv * Tl::kMatBytes + Tl::offset(row, ch)) = x;
+    }
+    if (tid < 2 * kPfTile) {
+      const int key = tid & (kPfTile - 1);
+      const int isv = tid >= kPfTile;
+      const float* raw = reinterpret_cast<const float*>(st + 2 * St::kCodeMat);
+      // raw layout: block w = key / 16 at floats 32 w (K) and 32 w + 16 (V)
+      const float x = raw[(key >> 4) * 32 + isv * 16 + (key & 15)];
+      const float y = key < valid ? x : 0.f;
+      (isv ? vsc : ksc)[key] = isv ? y : y * csc;
+    }
+  };
+
+  const int grp = lane >> 4;
+  const int tr_row = 4 * (grp >> 1) + ((lane & 15) >> 2);
+  const int tr_ch = 16 * (grp & 1) + 4 * (lane & 3);
+
+  bf16x8_t qb[NC];
+  {
+    const uint4* qv = reinterpret_cast<const uint4*>(a.q);
+    const size_t rowv = ((size_t)(q0 + tok) * a.h_q + kvh * g + hh) * (D / 8);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint4 x = row_ok ? qv[rowv + 2 * c + half] : make_uint4(0, 0, 0, 0);
+      x.x ^= qsign;
+      x.y ^= qsign;
+      x.z ^= qsign;
+      x.w ^= qsign;
+      qb[c] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+  issue_tile(0);
+  if (n_tiles > 1) issue_tile(1);
+  wait_vm<0>();
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    // Tile kt's copies landed (own ones: all but tile kt + 1's), then every
+    // wave's (barrier); every wave is also done with tile kt - 1.
+    if (kt + 1 < n_tiles) wait_vm<kCopies>();
+    else wait_vm<0>();
+    tile_barrier();
+    convert_tile(kt);
+    wait_lds();
+    tile_barrier();
+    if (kt + 2 < n_tiles) issue_tile(kt + 2);
+    if (!(wave_live && kt * kPfTile <= wave_pos_hi)) continue;
+
+    const int key0 = kt * kPfTile;
+    f32x16_t sc[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[h2][i] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint4 kx = *reinterpret_cast<const uint4*>(tile + Tl::offset(32 * h2 + col, 2 * c + half));
+        sc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx), qb[c],
+                                                         sc[h2], 0, 0, 0);
+      }
+    }
+    // The keys of accumulator elements (h2, 4j .. 4j + 3): 32 h2 + 8 j + 4 half + 0..3.
+    float kf[2][16], vf[2][16];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 k4 = *reinterpret_cast<const float4*>(ksc + 32 * h2 + 8 * j + 4 * half);
+        const float4 v4 = *reinterpret_cast<const float4*>(vsc + 32 * h2 + 8 * j + 4 * half);
+        kf[h2][4 * j + 0] = k4.x; kf[h2][4 * j + 1] = k4.y; kf[h2][4 * j + 2] = k4.z; kf[h2][4 * j + 3] = k4.w;
+        vf[h2][4 * j + 0] = v4.x; vf[h2][4 * j + 1] = v4.y; vf[h2][4 * j + 2] = v4.z; vf[h2][4 * j + 3] = v4.w;
+      }
+    // Scores in log2 units: the K scale (times |scale| log2 e) of each key.
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[h2][i] *= kf[h2][i];
+    if (key0 + kPfTile - 1 > wave_pos_lo) {
+      const int lim = pos - key0 - 4 * half;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * h2 + mfma32_row(i, 0) > lim) sc[h2][i] = kPfNegInf;
+    }
+    float tmax = kPfNegInf;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[h2][i]);
+    tmax = xor32_max(tmax);
+    if (__any(tmax > m + kPfSlack)) {
+      const float mn = tmax > m + kPfSlack ? tmax : m;
+      const float alpha = mn == m ? 1.f : fast_exp2(m - mn);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(sc[h2][i] - m);
+        ps += p;
+        sc[h2][i] = p * vf[h2][i];  // the weight times the key's V scale
+      }
+    lsum += ps;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x16_t& w = sc[c >> 1];
+      const int e0 = 8 * (c & 1);
+      uint4 pw;
+      pw.x = pack_bf16x2(w[e0 + 0], w[e0 + 1]);
+      pw.y = pack_bf16x2(w[e0 + 2], w[e0 + 3]);
+      pw.z = pack_bf16x2(w[e0 + 4], w[e0 + 5]);
+      pw.w = pack_bf16x2(w[e0 + 6], w[e0 + 7]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int chn = 32 * t + tr_ch;
+        const int ra = 16 * c + tr_row;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS i16x4_t*)(tile + Tl::kMatBytes + Tl::offset(ra, chn >> 3) + (chn & 4) * 2));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS i16x4_t*)(tile + Tl::kMatBytes + Tl::offset(ra + 8, chn >> 3) + (chn & 4) * 2));
+        const i16x4_t lohi[2] = {lo, hi};
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lohi), pb, o[t],
+                                                       0, 0, 0);
+      }
+    }
+  }
+
+  if (!row_ok) return;
+  const float lt = xor32_sum(lsum);
+  const float inv = 1.f / lt;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  const size_t orow = ((size_t)(q0 + tok) * a.h_q + kvh * g + hh) * D;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int chn = t * 32 + 8 * gq + 4 * half;
+      uint2 w;
+      w.x = pack_bf16x2(o[t][4 * gq + 0] * inv, o[t][4 * gq + 1] * inv);
+      w.y = pack_bf16x2(o[t][4 * gq + 2] * inv, o[t][4 * gq + 3] * inv);
+      *reinterpret_cast<uint2*>(&out[orow + chn]) = w;
+    }
+}
+
+static int compute_units_i8() {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    return n;
+  }();
+  return cus;
+}
+
+template <int D>
+static hipError_t launch_i8_d(const PrefillArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.max_q_len * a.g;
+  const int64_t gx = (rows + kPfRows - 1) / kPfRows;
+  const dim3 grid((unsigned)gx, a.h_kv, a.S);
+  // Sequence planes longest context first when the grid takes more than one
+  // round of the chip (as for the bf16 prefill).
+  PrefillArgs args = a;
+  const int cus = compute_units_i8();
+  args.longest_first = a.S > 1 && a.S <= kLptMaxSeqs && cus > 0 && gx * a.h_kv * a.S > cus;
+  hipLaunchKernelGGL((prefill_i8_kernel<D>), grid, dim3(256), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_i8(const PrefillArgs& a, int d_h, hipStream_t stream) {
+  if (d_h == 64) return launch_i8_d<64>(a, stream);
+  if (d_h == 128) return launch_i8_d<128>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

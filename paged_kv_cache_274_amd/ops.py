@@ -25,7 +25,7 @@ EXPORTED = ("kv_append", "paged_decode_attention", "paged_prefill_attention",
             "kv_append_int8", "paged_decode_attention_int8",
             "pkv_decode_workspace_bytes", "pkv_decode_num_splits", "pkv_status_string",
             "paged_decode_attention_split", "pkv_decode_workspace_bytes_split",
-            "paged_decode_attention_noalloc",
+            "paged_decode_attention_noalloc", "paged_prefill_attention_int8",
             "copy_blocks", "swap_blocks",
             "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_sequence", "pkv_bm_append",
             "pkv_bm_fork", "pkv_bm_free", "pkv_bm_swap_out", "pkv_bm_swap_in",
@@ -94,6 +94,9 @@ def lib() -> ctypes.CDLL:
                                               i32, i32, i32, i32, ctypes.c_float, i32, vp,
                                               ctypes.c_size_t, vp]
     L.paged_decode_attention_int8.restype = i32
+    L.paged_prefill_attention_int8.argtypes = [vp, vp, i32p, vp, vp, vp, vp, i32p, i32p, i32, i32,
+                                               i32, i32, i32, i32, i32, i32, ctypes.c_float, vp]
+    L.paged_prefill_attention_int8.restype = i32
     ptrs = ctypes.POINTER(ctypes.c_void_p)
     sizes = ctypes.POINTER(ctypes.c_int64)
     L.copy_blocks.argtypes = [ptrs, sizes, i32, i32, i32p, i32, vp]
@@ -422,6 +425,55 @@ def bind_prefill(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache: torch.Ten
         rc = fn(*args)
         if rc != 0:
             raise PkvError("paged_prefill_attention", rc)
+        return out
+    return call
+
+
+def paged_prefill_attention_int8(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                                 k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 k_scale: torch.Tensor, v_scale: torch.Tensor,
+                                 block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                 max_q_len: int, scale: Optional[float] = None,
+                                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal chunked prefill over the INT8 cache.  q, out: bf16 packed [T_q, h_q, d_h]."""
+    return bind_prefill_int8(q, cu_seqlens_q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                             context_lens, max_q_len, scale, out)()
+
+
+def bind_prefill_int8(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, max_q_len: int,
+                      scale: Optional[float] = None, out: Optional[torch.Tensor] = None):
+    """paged_prefill_attention_int8 with its arguments checked and marshalled
+    once: returns a call that launches it (on the stream current now)."""
+    n_blocks, h_kv, d = _pool_shape(k_cache, v_cache)
+    _need(k_cache.dtype == torch.int8, "the INT8 pools must be int8")
+    _scale_pools(k_scale, v_scale, n_blocks, h_kv)
+    _need(q.dim() == 3 and q.shape[2] == d and q.dtype == torch.bfloat16,
+          "q must be bf16 [T_q, h_q, d_h]")
+    T_q, h_q = int(q.shape[0]), int(q.shape[1])
+    S = int(context_lens.shape[0])
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.shape == (S + 1,),
+          "cu_seqlens_q must be int32 [S + 1]")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == S, "block_tables must be int32 [S, max_blocks]")
+    _need(context_lens.dtype == torch.int32, "context_lens must be int32 [S]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _dev(q, cu_seqlens_q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    fn = lib().paged_prefill_attention_int8
+    args = (out.data_ptr(), q.data_ptr(), cu_seqlens_q.data_ptr(), k_cache.data_ptr(),
+            v_cache.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(), block_tables.data_ptr(),
+            context_lens.data_ptr(), S, T_q, int(max_q_len), h_q, h_kv, d, n_blocks,
+            int(block_tables.shape[1]), float(scale), _stream(q))
+
+    def call() -> torch.Tensor:
+        rc = fn(*args)
+        if rc != 0:
+            raise PkvError("paged_prefill_attention_int8", rc)
         return out
     return call
 

@@ -238,6 +238,26 @@ def test_decode_int8_validation():
                                             16, 256, 0.1, 2, FAKE, 1 << 30, None) == 1
 
 
+def _prefill8(**kw):
+    a = dict(out=FAKE, q=FAKE, cu=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, tbl=FAKE, lens=FAKE,
+             S=2, T_q=10, mq=8, h_q=14, h_kv=2, d=64, nb=64, mb=16, scale=0.125)
+    a.update(kw)
+    return ops.lib().paged_prefill_attention_int8(
+        a["out"], a["q"], a["cu"], a["kc"], a["vc"], a["ks"], a["vs"], a["tbl"], a["lens"],
+        a["S"], a["T_q"], a["mq"], a["h_q"], a["h_kv"], a["d"], a["nb"], a["mb"], a["scale"], None)
+
+
+def test_prefill_int8_validation():
+    assert _prefill8(ks=None) == 1
+    assert _prefill8(vs=FAKE + 4) == 1
+    assert _prefill8(kc=MISALIGNED) == 1
+    assert _prefill8(h_q=15) == 1
+    assert _prefill8(d=32) == 2
+    assert _prefill8(scale=float("inf")) == 1
+    assert _prefill8(S=0, out=None) == 0
+    assert _prefill8(T_q=0, out=None) == 0
+
+
 def _ptrs(*vals):
     return (ctypes.c_void_p * len(vals))(*vals)
 

@@ -289,6 +289,45 @@ def test_prefill_grid(d, h_q, h_kv, seqs):
     check_prefill(w, res, kc_ref, vc_ref)
 
 
+@pytest.mark.parametrize("d,h_q,h_kv,seqs", [
+    (128, 32, 8, [(512, 512)] * 16),
+    (64, 14, 2, [(512, 512)] * 40),
+    (128, 32, 8, [(1500, 300)] * 8 + [(1300, 301)] * 8),   # chunks starting mid-tile
+])
+def test_prefill_full_prompts_many_rounds(d, h_q, h_kv, seqs):
+    """Whole and chunked prompts on grids of several rounds of the chip (the
+    software-pipelined key walk with four tile buffers, longest context first)."""
+    rng = np.random.default_rng(2100 + d + len(seqs))
+    w = W.build("rb2", rng, dtype="bf16", h_q=h_q, h_kv=h_kv, d=d, prefill=seqs,
+                free_frac=0.1, poison=True)
+    res = run(w, DEV)
+    kc_ref, vc_ref = check_append(w, res)
+    check_prefill(w, res, kc_ref, vc_ref)
+
+
+@pytest.mark.parametrize("shape", [(32, 8, 128), (14, 2, 64)])
+def test_prefill_long_prompts_sampled(shape):
+    """The bench's long-prompt workload (4 causal prompts of 4096 tokens) in
+    the launch the bench times, checked on sampled query rows: row p of a
+    prompt is the oracle's prefill of that one query at position p over keys
+    0..p."""
+    w = W.long_prefill(*shape)
+    res = run(w, DEV, do_decode=False)
+    kc_ref, vc_ref = O.kv_append(pins.np64(w.k_new), pins.np64(w.v_new), w.slot_mapping.numpy(),
+                                 pins.np64(w.k_cache), pins.np64(w.v_cache))
+    rng = np.random.default_rng(9)
+    err = 0.0
+    for s in range(w.S):
+        for p in [0, 1, 63, 64, 127, 2048, 4094, 4095] + [int(x) for x in rng.integers(0, 4096, 3)]:
+            r = int(w.pre_cu_seqlens[s]) + p
+            ref = O.prefill(pins.np64(w.pre_q[r:r + 1]), np.array([0, 1], np.int32), kc_ref,
+                            vc_ref, w.pre_block_tables[s:s + 1].numpy(),
+                            np.array([p + 1], np.int32), w.scale)
+            err = max(err, max_err(res.prefill[r:r + 1], ref))
+    print(f"long prompts {shape}: sampled max|err| {err:.3e}")
+    assert err <= 2e-2
+
+
 @pytest.mark.parametrize("n_s", [2, 4, 5])
 def test_multi_token_decode_verify(n_s):
     """Multi-token decode (a speculative verify step: the n_s newest tokens of

@@ -177,3 +177,83 @@ def test_decode_int8_query_magnitudes(q_mag):
         out = _decode(w, [t.to(DEV) for t in got], splits)
         err = max_err(out, _oracle_decode(w, ref))
         assert err <= TOL, f"int8 decode max|err| {err} at |q| ~ {q_mag}"
+
+
+# ----------------------------------------------------------------------------- prefill
+
+def _prefill(w, pools_dev):
+    out = ops.paged_prefill_attention_int8(
+        w.pre_q.to(DEV), w.pre_cu_seqlens.to(DEV), *pools_dev, w.pre_block_tables.to(DEV),
+        w.pre_context_lens.to(DEV), w.pre_max_q_len, scale=w.scale)
+    return out.cpu()
+
+
+def _oracle_prefill(w, ref):
+    return Q.prefill_int8(pins.np64(w.pre_q), w.pre_cu_seqlens.numpy(), *ref,
+                          w.pre_block_tables.numpy(), w.pre_context_lens.numpy(), w.scale)
+
+
+PREFILL8 = [
+    # name, d, h_q, h_kv, [(context, n_new)]
+    ("config-5 prompts", 64, 14, 2, [(512, 512)] * 4),
+    ("chunks cut mid-tile", 128, 32, 8, [(1500, 300), (700, 700), (90, 33), (17, 16)]),
+    ("gqa 8, ragged", 128, 8, 1, [(150, 150), (260, 130), (1, 1)]),
+    ("d 64, long chunk", 64, 16, 2, [(2100, 1000), (48, 48)]),
+]
+
+
+@pytest.mark.parametrize("name,d,h_q,h_kv,seqs", PREFILL8, ids=[p[0] for p in PREFILL8])
+def test_prefill_int8_matches_oracle(name, d, h_q, h_kv, seqs):
+    """Causal chunked prefill over the INT8 cache (appended this step by
+    kv_append_int8; unused slots' scales NaN) against the oracle's prefill over
+    the dequantised cache."""
+    rng = np.random.default_rng(400 + d + h_q + len(seqs))
+    w = W.build("pre8", rng, dtype="bf16", h_q=h_q, h_kv=h_kv, d=d, prefill=seqs,
+                free_frac=0.2, poison=True)
+    p8 = W.int8_pools(w, seed=41, poison=True)
+    got, ref = _append(w, p8)
+    _check_append_exact(got, ref)
+    out = _prefill(w, [t.to(DEV) for t in got])
+    err = max_err(out, _oracle_prefill(w, ref))
+    print(f"int8 prefill {name}: max|err| {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("n_s", [2, 4, 5])
+def test_verify_over_int8_cache(n_s):
+    """Multi-token decode (the n_s newest tokens of each sequence, decode-shaped
+    contexts) over the INT8 cache; the last row equals the one-token INT8
+    decode of the same context."""
+    rng = np.random.default_rng(450 + n_s)
+    lens = [int(x) for x in rng.integers(128, 4096, size=12, endpoint=True)] + [n_s, 16 + n_s]
+    w = W.build("verify8", rng, dtype="bf16", h_q=32, h_kv=8, d=128,
+                prefill=[(L, n_s) for L in lens], free_frac=0.1, poison=True)
+    p8 = W.int8_pools(w, seed=42, poison=True)
+    got, ref = _append(w, p8)
+    dev = [t.to(DEV) for t in got]
+    out = _prefill(w, dev)
+    err = max_err(out, _oracle_prefill(w, ref))
+    last = w.pre_cu_seqlens[1:].long() - 1
+    one = ops.paged_decode_attention_int8(w.pre_q[last].to(DEV), *dev,
+                                          w.pre_block_tables.to(DEV),
+                                          w.pre_context_lens.to(DEV), max(lens),
+                                          scale=w.scale).cpu()
+    print(f"int8 verify n_s={n_s}: max|err| {err:.3e}")
+    assert err <= TOL
+    assert max_err(out[last], one.double().numpy()) <= TOL
+
+
+@pytest.mark.parametrize("S", [40, 300])
+def test_prefill_int8_beyond_one_round(S):
+    """Grids of more workgroups than the chip holds: sequence planes taken
+    longest context first (S <= 256) or in index order (S = 300)."""
+    rng = np.random.default_rng(470 + S)
+    lens = [max(3, int(x)) for x in rng.integers(3, 1500, size=S)]
+    w = W.build("many8", rng, dtype="bf16", h_q=16, h_kv=8, d=128,
+                prefill=[(L, 3) for L in lens], free_frac=0.05, poison=True)
+    p8 = W.int8_pools(w, seed=43, poison=True)
+    got, ref = _append(w, p8)
+    out = _prefill(w, [t.to(DEV) for t in got])
+    err = max_err(out, _oracle_prefill(w, ref))
+    print(f"int8 prefill, {S} sequences: max|err| {err:.3e}")
+    assert err <= TOL

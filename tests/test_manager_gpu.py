@@ -298,3 +298,49 @@ def test_int8_cache_under_the_manager():
         err = max(err, max_err(out.cpu(), want))
     print(f"int8 cache under the manager: decode max|err| = {err:.3e}")
     assert err <= TOL
+
+
+def test_int8_prefill_after_prefix_hit():
+    """An INT8 cache under the manager: the second request sharing a 100-token
+    system prompt is served 100 tokens from the cache (one copy on write of the
+    partly shared block), and the INT8 prefill of its other 45 tokens over the
+    shared and copied blocks is within 2e-2 of the oracle's prefill over the
+    dequantised cache."""
+    import oracle.blocks as OB
+    import oracle.quant as Q
+    rng = np.random.default_rng(274106)
+    q_rng = np.random.default_rng(274107)
+    n_blocks = 40
+    bm = ops.BlockManager(n_blocks)
+    dev_pools = [torch.zeros((n_blocks, H_KV, 16, D), dtype=torch.int8, device=DEV),
+                 torch.zeros((n_blocks, H_KV, 16, D), dtype=torch.int8, device=DEV),
+                 torch.full((n_blocks, H_KV, 16), float("nan"), device=DEV),
+                 torch.full((n_blocks, H_KV, 16), float("nan"), device=DEV)]
+    ref = [p.cpu().numpy() for p in dev_pools]
+    system = list(rng.integers(0, VOCAB, 100))
+    err = 0.0
+    for sid, extra in ((1, 30), (2, 45)):
+        toks = system + list(rng.integers(0, VOCAB, extra))
+        n_cached, slots, cow = bm.add_sequence(sid, toks)
+        if len(cow):
+            ops.copy_blocks(dev_pools, torch.from_numpy(cow).to(DEV))
+            ref = OB.copy_blocks(ref, ref, cow)
+        k, v = kv_rows(toks, 0)
+        ops.kv_append_int8(k.to(DEV), v.to(DEV), torch.from_numpy(slots).to(DEV), *dev_pools)
+        ref = list(Q.kv_append_int8(k.float().numpy(), v.float().numpy(), slots, *ref))
+        n_new = len(toks) - n_cached
+        tbl, lens = bm.block_tables([sid])
+        q = torch.from_numpy(q_rng.standard_normal((n_new, H_Q, D)).astype(np.float32)).to(
+            torch.bfloat16)
+        cu = np.array([0, n_new], np.int32)
+        out = ops.paged_prefill_attention_int8(q.to(DEV), torch.from_numpy(cu).to(DEV),
+                                               *dev_pools, torch.from_numpy(tbl).to(DEV),
+                                               torch.from_numpy(lens).to(DEV), n_new,
+                                               scale=SCALE)
+        torch.cuda.synchronize()
+        want = Q.prefill_int8(q.to(torch.float64).numpy(), cu, *ref, tbl, lens, SCALE)
+        err = max(err, max_err(out.cpu(), want))
+        if sid == 2:
+            assert n_cached == 100 and n_new == 45 and len(cow) == 1
+    print(f"int8 prefill after a prefix hit: max|err| = {err:.3e}")
+    assert err <= TOL

@@ -189,7 +189,10 @@ __global__ __launch_bounds__(256 * KS) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
     }
-    const float mn = m;
+    // A row whose keys so far were all masked (possible for the second key
+    // group, which starts at tile 1) keeps m = -inf; its scores are all -inf,
+    // and a finite reference gives them weight 0 instead of -inf + inf.
+    const float mn = m == kPfNegInf ? 0.f : m;
     float ps = 0.f;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
@@ -337,6 +340,247 @@ __global__ __launch_bounds__(256 * KS) void prefill_bf16_kernel(PrefillArgs a) {
     }
 }
 
+// Few query rows per (sequence, KV head): at most 32 packed rows (multi-token
+// decode: a few new tokens times the GQA group), all held by every wave of the
+// workgroup.  The key walk is split over the 4 waves instead of the rows: wave
+// w attends the 32-key chunks w, w + 4, w + 8, ... of the context, each copied
+// from HBM into the wave's own two LDS stages (one chunk in flight while the
+// other is used), so the waves need no barrier until the end, where their
+// softmax states are merged through LDS.  Four waves walk a context four times
+// faster than the one wave that holds the rows in prefill_bf16_kernel.
+constexpr int kFewKeys = 32;
+template <int D>
+__global__ __launch_bounds__(256) void prefill_few_rows_kernel(PrefillArgs a) {
+  using Tl = PfTile<D>;
+  constexpr int kStage = 2 * kFewKeys * Tl::kRowBytes;  // K then V of one chunk
+  constexpr int kWaveBytes = 2 * kStage;
+  constexpr int NC = D / 16;
+  constexpr int NT = D / 32;
+  constexpr int kCopies = 2 * 2 * Tl::kCopiesPerBlock;  // K and V of two blocks
+  constexpr int kFields = NT * 16 + 2;                  // merge: O^T, m, l per lane
+  __shared__ __attribute__((aligned(16))) unsigned char
+      lds[(kPfWaves * kWaveBytes > kPfWaves * kFields * 256) ? kPfWaves * kWaveBytes
+                                                             : kPfWaves * kFields * 256];
+
+  const int s = a.longest_first ? longest_first_sequence(a, blockIdx.z) : (int)blockIdx.z;
+  const int kvh = blockIdx.y;
+  const int g = a.g;
+  const int q0 = a.cu_seqlens_q[s];
+  const int n = a.cu_seqlens_q[s + 1] - q0;
+  int L = a.context_lens[s];
+  L = max(0, min(L, a.max_blocks_per_seq * kBlock));
+  const int rows = n * g;
+  if (n <= 0 || n > L || rows > 32 || q0 < 0 || q0 + n > a.T_q) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int first = L - n;
+  const bool row_ok = col < rows;
+  const int tok = row_ok ? col / g : n - 1;
+  const int hh = row_ok ? col - (col / g) * g : 0;
+  const int pos = first + tok;
+  const int Lu = uniform(L);
+  const int n_chunks = (Lu + kFewKeys - 1) / kFewKeys;
+
+  const float csc = fabsf(a.scale_log2);
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  f32x16_t o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+  float m = kPfNegInf;
+  float lsum = 0.f;
+
+  const unsigned char* kc = reinterpret_cast<const unsigned char*>(a.k_cache);
+  const unsigned char* vc = reinterpret_cast<const unsigned char*>(a.v_cache);
+  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  const size_t head_bytes = (size_t)kBlock * Tl::kRowBytes;
+  unsigned char* const mine = lds + wave * kWaveBytes;
+
+  // Copies the two blocks of chunk c (keys 32c .. 32c + 31), K and V, into
+  // stage st of this wave (rows = keys of the chunk, swizzled as PfTile).
+  auto issue_chunk = [&](int c, int st) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int bi = min(2 * c + b, a.max_blocks_per_seq - 1);
+      int blk = constant_view(trow)[bi];
+      blk = (blk >= 0 && blk < a.n_blocks) ? blk : 0;
+      const size_t gbase = ((size_t)blk * a.h_kv + kvh) * head_bytes;
+#pragma unroll
+      for (int i = 0; i < Tl::kCopiesPerBlock; ++i) {
+        const int rb = i * Tl::kRowsPerCopy + lane / Tl::kChunks;  // row within the block
+        const int row = b * kBlock + rb;                            // row within the chunk
+        const int chunk = (lane % Tl::kChunks) ^ Tl::swz(row);
+        const size_t src = gbase + (size_t)rb * Tl::kRowBytes + chunk * 16;
+        const int ldst = (b * kBlock + i * Tl::kRowsPerCopy) * Tl::kRowBytes;
+        copy_to_lds(kc + src, mine + st * kStage + ldst);
+        copy_to_lds(vc + src, mine + st * kStage + kFewKeys * Tl::kRowBytes + ldst);
+      }
+    }
+  };
+
+  bf16x8_t qb[NC];
+  {
+    const uint4* qv = reinterpret_cast<const uint4*>(a.q);
+    const size_t rowv = ((size_t)(q0 + tok) * a.h_q + kvh * g + hh) * (D / 8);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint4 x = row_ok ? qv[rowv + 2 * c + half] : make_uint4(0, 0, 0, 0);
+      x.x ^= qsign;
+      x.y ^= qsign;
+      x.z ^= qsign;
+      x.w ^= qsign;
+      qb[c] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+
+  const int grp = lane >> 4;
+  const int tr_row = 4 * (grp >> 1) + ((lane & 15) >> 2);
+  const int tr_ch = 16 * (grp & 1) + 4 * (lane & 3);
+
+  if (wave < n_chunks) issue_chunk(wave, 0);
+  for (int c = wave, st = 0; c < n_chunks; c += kPfWaves, st ^= 1) {
+    const bool more = c + kPfWaves < n_chunks;
+    if (more) issue_chunk(c + kPfWaves, st ^ 1);
+    // This wave's copies of chunk c have landed (the next chunk's may stay in
+    // flight); no other wave reads them.
+    if (more)
+      wait_vm<kCopies>();
+    else
+      wait_vm<0>();
+    const unsigned char* kb = mine + st * kStage;
+    unsigned char* vb = mine + st * kStage + kFewKeys * Tl::kRowBytes;
+    const int key0 = c * kFewKeys;
+    if (key0 + kFewKeys > Lu) {
+      // V rows past the context of the last chunk are zeroed (own stage).
+      const int zr = Lu - key0;
+      for (int z = lane; z < (kFewKeys - zr) * Tl::kChunks; z += 64)
+        *reinterpret_cast<uint4*>(vb + (zr + z / Tl::kChunks) * Tl::kRowBytes + (z % Tl::kChunks) * 16) =
+            make_uint4(0, 0, 0, 0);
+      wait_lds();
+    }
+    f32x16_t sc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+#pragma unroll
+    for (int c2 = 0; c2 < NC; ++c2) {
+      const uint4 kx = *reinterpret_cast<const uint4*>(kb + Tl::offset(col, 2 * c2 + half));
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx), qb[c2], sc, 0,
+                                                   0, 0);
+    }
+    if (key0 + kFewKeys - 1 > first) {
+      const int lim = pos - key0 - 4 * half;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (mfma32_row(i, 0) > lim) sc[i] = kPfNegInf;
+    }
+    float tmax = kPfNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[i]);
+    tmax = xor32_max(tmax) * csc;
+    if (__any(tmax > m + kPfSlack)) {
+      const float mn = tmax > m + kPfSlack ? tmax : m;
+      const float alpha = mn == m ? 1.f : fast_exp2(m - mn);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+    }
+    // A wave's first chunk can lie wholly past a row's position (m stays
+    // -inf, all its scores -inf): a finite reference gives them weight 0.
+    const float mb = m == kPfNegInf ? 0.f : m;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(sc[i], csc, -mb));
+      sc[i] = p;
+      ps += p;
+    }
+    lsum += ps;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      // P^T for keys 16 c2 .. 16 c2 + 15: accumulator elements 8 c2 .. 8 c2 + 7.
+      uint4 pw;
+      pw.x = pack_bf16x2(sc[8 * c2 + 0], sc[8 * c2 + 1]);
+      pw.y = pack_bf16x2(sc[8 * c2 + 2], sc[8 * c2 + 3]);
+      pw.z = pack_bf16x2(sc[8 * c2 + 4], sc[8 * c2 + 5]);
+      pw.w = pack_bf16x2(sc[8 * c2 + 6], sc[8 * c2 + 7]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int ch = 32 * t + tr_ch;
+        const int ra = 16 * c2 + tr_row;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS i16x4_t*)(vb + Tl::offset(ra, ch >> 3) + (ch & 4) * 2));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS i16x4_t*)(vb + Tl::offset(ra + 8, ch >> 3) + (ch & 4) * 2));
+        const i16x4_t lohi[2] = {lo, hi};
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lohi), pb, o[t],
+                                                       0, 0, 0);
+      }
+    }
+    // Every LDS read of this stage is done before the stage is refilled by
+    // the copy issued at the top of the iteration after next.
+    wait_lds();
+  }
+
+  // Merge the four waves' states for the same rows through LDS (field f of
+  // lane l of wave w at float (f * 4 + w) * 64 + l), in wave 0.
+  float* mg = reinterpret_cast<float*>(lds);
+  auto at = [&](int f, int w) -> float& { return mg[(f * kPfWaves + w) * 64 + lane]; };
+  tile_barrier();  // every wave is done with its stages
+  if (wave != 0) {
+    at(0, wave) = m;
+    at(1, wave) = lsum;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) at(2 + t * 16 + e, wave) = o[t][e];
+  }
+  wait_lds();
+  tile_barrier();
+  if (wave != 0 || !row_ok) return;
+  float mm = m;
+#pragma unroll
+  for (int w = 1; w < kPfWaves; ++w) mm = fmaxf(mm, at(0, w));
+  const float a0 = m == kPfNegInf ? 0.f : fast_exp2(m - mm);
+  lsum *= a0;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[t][e] *= a0;
+#pragma unroll
+  for (int w = 1; w < kPfWaves; ++w) {
+    const float mw = at(0, w);
+    const float aw = mw == kPfNegInf ? 0.f : fast_exp2(mw - mm);
+    lsum += at(1, w) * aw;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[t][e] += at(2 + t * 16 + e, w) * aw;
+  }
+  const float lt = xor32_sum(lsum);
+  const float inv = 1.f / lt;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  const size_t orow = ((size_t)(q0 + tok) * a.h_q + kvh * g + hh) * D;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int ch = t * 32 + 8 * gq + 4 * half;
+      uint2 w;
+      w.x = pack_bf16x2(o[t][4 * gq + 0] * inv, o[t][4 * gq + 1] * inv);
+      w.y = pack_bf16x2(o[t][4 * gq + 2] * inv, o[t][4 * gq + 3] * inv);
+      *reinterpret_cast<uint2*>(&out[orow + ch]) = w;
+    }
+}
+
 static int compute_units() {
   static const int cus = [] {
     int dev = 0, n = 0;
@@ -351,6 +595,16 @@ static int compute_units() {
 template <int D>
 static hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.max_q_len * a.g;
+#ifndef PKV_PF_NO_FEW
+  if (rows <= 32) {
+    const dim3 grid(1, a.h_kv, a.S);
+    PrefillArgs args = a;
+    const int cus = compute_units();
+    args.longest_first = a.S > 1 && a.S <= kLptMaxSeqs && cus > 0 && (int64_t)a.h_kv * a.S > cus;
+    hipLaunchKernelGGL((prefill_few_rows_kernel<D>), grid, dim3(256), 0, stream, args);
+    return hipGetLastError();
+  }
+#endif
   const int64_t gx = (rows + kPfRows - 1) / kPfRows;
   const dim3 grid((unsigned)gx, a.h_kv, a.S);
   // Order the sequence planes longest first when the grid takes more than one

@@ -56,8 +56,9 @@ __device__ __forceinline__ void copy_to_lds(const void* src, const void* lds_dst
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  // vmcnt is 6 bits: the low 4 in bits 3:0, the high 2 in bits 15:14.
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 // s_waitcnt lgkmcnt(0): this wave's LDS stores are done.
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }

@@ -258,12 +258,13 @@ __global__ __launch_bounds__(256) void prefill_i8_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
     }
+    const float mb = m == kPfNegInf ? 0.f : m;  // all scores so far masked: weight 0
     float ps = 0.f;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(sc[h2][i] - m);
+        const float p = fast_exp2(sc[h2][i] - mb);
         ps += p;
         sc[h2][i] = p * vf[h2][i];  // the weight times the key's V scale
       }

@@ -276,6 +276,10 @@ PREFILL_GRID = [
     # many 64-key tiles, ragged context tails, chunks that start mid-tile
     (128, 32, 8, [(3000, 700), (2049, 2049)]),
     (64, 14, 2, [(4096, 64), (777, 777), (1, 1)]),
+    # a chunk whose rows straddle key 64 in a small grid: the second key group
+    # starts at tile 1, wholly past some rows' positions
+    (64, 14, 2, [(100, 60)]),
+    (64, 16, 2, [(90, 50), (70, 70)]),
 ]
 
 

@@ -311,6 +311,278 @@ __global__ __launch_bounds__(256) void prefill_i8_kernel(PrefillArgs a) {
     }
 }
 
+// Few query rows per (sequence, KV head) (at most 32: multi-token decode), as
+// prefill_few_rows_kernel in prefill.hip: the 4 waves split the key walk into
+// 32-key chunks w, w + 4, ..., each wave staging its chunk's codes and scales
+// in two LDS stages of its own (one in flight) and widening them itself into
+// its own bf16 chunk, so no barrier is needed until the states are merged.
+constexpr int kI8FewKeys = 32;
+template <int D>
+__global__ __launch_bounds__(256) void prefill_i8_few_rows_kernel(PrefillArgs a) {
+  using Tl = PfTile<D>;
+  constexpr int kCodes = kI8FewKeys * D;                       // codes of K (or V) of a chunk
+  constexpr int kStage = 2 * kCodes + 2 * kI8FewKeys * 4;       // codes + raw K, V scales
+  constexpr int kChunkBf = 2 * kI8FewKeys * Tl::kRowBytes;      // bf16 K then V
+  constexpr int kWaveBytes = 2 * kStage + kChunkBf + 2 * kI8FewKeys * 4;
+  constexpr int NC = D / 16;
+  constexpr int NT = D / 32;
+  constexpr int kCopiesPerBlock = kBlock * D / 1024;
+  constexpr int kCopies = 2 * 2 * kCopiesPerBlock + 2;         // codes of 2 blocks, 2 scale copies
+  constexpr int kFields = NT * 16 + 2;
+  __shared__ __attribute__((aligned(16))) unsigned char
+      lds[(kPfWaves * kWaveBytes > kPfWaves * kFields * 256) ? kPfWaves * kWaveBytes
+                                                             : kPfWaves * kFields * 256];
+
+  const int s = a.longest_first ? longest_first_sequence(a, blockIdx.z) : (int)blockIdx.z;
+  const int kvh = blockIdx.y;
+  const int g = a.g;
+  const int q0 = a.cu_seqlens_q[s];
+  const int n = a.cu_seqlens_q[s + 1] - q0;
+  int L = a.context_lens[s];
+  L = max(0, min(L, a.max_blocks_per_seq * kBlock));
+  const int rows = n * g;
+  if (n <= 0 || n > L || rows > 32 || q0 < 0 || q0 + n > a.T_q) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int first = L - n;
+  const bool row_ok = col < rows;
+  const int tok = row_ok ? col / g : n - 1;
+  const int hh = row_ok ? col - (col / g) * g : 0;
+  const int pos = first + tok;
+  const int Lu = __builtin_amdgcn_readfirstlane(L);
+  const int n_chunks = (Lu + kI8FewKeys - 1) / kI8FewKeys;
+
+  const float csc = fabsf(a.scale_log2);
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  f32x16_t o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+  float m = kPfNegInf;
+  float lsum = 0.f;
+
+  const unsigned char* kc = reinterpret_cast<const unsigned char*>(a.k_cache);
+  const unsigned char* vc = reinterpret_cast<const unsigned char*>(a.v_cache);
+  const unsigned char* ks = reinterpret_cast<const unsigned char*>(a.k_scale);
+  const unsigned char* vs = reinterpret_cast<const unsigned char*>(a.v_scale);
+  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  unsigned char* const mine = lds + wave * kWaveBytes;
+  unsigned char* const cbf = mine + 2 * kStage;                          // bf16 chunk
+  float* const ksc = reinterpret_cast<float*>(cbf + kChunkBf);          // sanitised scales
+  float* const vsc = ksc + kI8FewKeys;
+
+  // Copies chunk c (blocks 2c, 2c + 1): codes of K then V (rows = keys, D
+  // bytes each), then the blocks' K and V scales (16 each, lanes 0-3 / 4-7 of
+  // one copy per block: block b at floats 32 b .. 32 b + 31, K then V).
+  auto issue_chunk = [&](int c, int st) {
+    unsigned char* dst = mine + st * kStage;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int bi = min(2 * c + b, a.max_blocks_per_seq - 1);
+      int blk = constant_view(trow)[bi];
+      blk = (blk >= 0 && blk < a.n_blocks) ? blk : 0;
+      const size_t bh = (size_t)blk * a.h_kv + kvh;
+#pragma unroll
+      for (int i = 0; i < kCopiesPerBlock; ++i) {
+        const size_t src = bh * (kBlock * D) + (size_t)i * 1024 + lane * 16;
+        const int d = b * kBlock * D + i * 1024;
+        copy_to_lds(kc + src, dst + d);
+        copy_to_lds(vc + src, dst + kCodes + d);
+      }
+      if (lane < 8) {
+        const unsigned char* src = (lane < 4 ? ks : vs) + bh * (kBlock * 4) + (lane & 3) * 16;
+        copy_to_lds(src, dst + 2 * kCodes + b * 128);
+      }
+    }
+  };
+  // Widens chunk c (stage st) into this wave's bf16 chunk and sanitised scales.
+  auto convert_chunk = [&](int c, int st) {
+    const unsigned char* src = mine + st * kStage;
+    const int valid = Lu - c * kI8FewKeys;
+    constexpr int kUnits = 2 * kI8FewKeys * Tl::kChunks;
+#pragma unroll
+    for (int u0 = 0; u0 < kUnits; u0 += 64) {
+      const int u = u0 + lane;
+      const int isv = u >= kI8FewKeys * Tl::kChunks;
+      const int uu = isv ? u - kI8FewKeys * Tl::kChunks : u;
+      const int row = uu / Tl::kChunks;
+      const int ch = uu - row * Tl::kChunks;
+      const uint2 w = *reinterpret_cast<const uint2*>(src + isv * kCodes + row * D + ch * 8);
+      uint4 x;
+      widen4(w.x, x.x, x.y);
+      widen4(w.y, x.z, x.w);
+      if (isv && row >= valid) x = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(cbf + isv * kI8FewKeys * Tl::kRowBytes + Tl::offset(row, ch)) = x;
+    }
+    {
+      const int key = lane & (kI8FewKeys - 1);
+      const int isv = lane >= kI8FewKeys;
+      const float* raw = reinterpret_cast<const float*>(src + 2 * kCodes);
+      const float x = raw[(key >> 4) * 32 + isv * 16 + (key & 15)];
+      const float y = key < valid ? x : 0.f;
+      (isv ? vsc : ksc)[key] = isv ? y : y * csc;
+    }
+    wait_lds();
+  };
+
+  bf16x8_t qb[NC];
+  {
+    const uint4* qv = reinterpret_cast<const uint4*>(a.q);
+    const size_t rowv = ((size_t)(q0 + tok) * a.h_q + kvh * g + hh) * (D / 8);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint4 x = row_ok ? qv[rowv + 2 * c + half] : make_uint4(0, 0, 0, 0);
+      x.x ^= qsign;
+      x.y ^= qsign;
+      x.z ^= qsign;
+      x.w ^= qsign;
+      qb[c] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+  const int grp = lane >> 4;
+  const int tr_row = 4 * (grp >> 1) + ((lane & 15) >> 2);
+  const int tr_ch = 16 * (grp & 1) + 4 * (lane & 3);
+
+  if (wave < n_chunks) issue_chunk(wave, 0);
+  for (int c = wave, st = 0; c < n_chunks; c += kPfWaves, st ^= 1) {
+    const bool more = c + kPfWaves < n_chunks;
+    if (more) issue_chunk(c + kPfWaves, st ^ 1);
+    if (more)
+      wait_vm<kCopies>();
+    else
+      wait_vm<0>();
+    convert_chunk(c, st);
+    const int key0 = c * kI8FewKeys;
+    f32x16_t sc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+#pragma unroll
+    for (int c2 = 0; c2 < NC; ++c2) {
+      const uint4 kx = *reinterpret_cast<const uint4*>(cbf + Tl::offset(col, 2 * c2 + half));
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx), qb[c2], sc, 0,
+                                                   0, 0);
+    }
+    // Keys of accumulator elements 4j .. 4j + 3: 8 j + 4 half + 0..3.
+    float kf[16], vf[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 k4 = *reinterpret_cast<const float4*>(ksc + 8 * j + 4 * half);
+      const float4 v4 = *reinterpret_cast<const float4*>(vsc + 8 * j + 4 * half);
+      kf[4 * j + 0] = k4.x; kf[4 * j + 1] = k4.y; kf[4 * j + 2] = k4.z; kf[4 * j + 3] = k4.w;
+      vf[4 * j + 0] = v4.x; vf[4 * j + 1] = v4.y; vf[4 * j + 2] = v4.z; vf[4 * j + 3] = v4.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] *= kf[i];
+    if (key0 + kI8FewKeys - 1 > first) {
+      const int lim = pos - key0 - 4 * half;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (mfma32_row(i, 0) > lim) sc[i] = kPfNegInf;
+    }
+    float tmax = kPfNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[i]);
+    tmax = xor32_max(tmax);
+    if (__any(tmax > m + kPfSlack)) {
+      const float mn = tmax > m + kPfSlack ? tmax : m;
+      const float alpha = mn == m ? 1.f : fast_exp2(m - mn);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+    }
+    const float mb = m == kPfNegInf ? 0.f : m;  // all scores so far masked: weight 0
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(sc[i] - mb);
+      ps += p;
+      sc[i] = p * vf[i];
+    }
+    lsum += ps;
+    const unsigned char* vb = cbf + kI8FewKeys * Tl::kRowBytes;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      uint4 pw;
+      pw.x = pack_bf16x2(sc[8 * c2 + 0], sc[8 * c2 + 1]);
+      pw.y = pack_bf16x2(sc[8 * c2 + 2], sc[8 * c2 + 3]);
+      pw.z = pack_bf16x2(sc[8 * c2 + 4], sc[8 * c2 + 5]);
+      pw.w = pack_bf16x2(sc[8 * c2 + 6], sc[8 * c2 + 7]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int chn = 32 * t + tr_ch;
+        const int ra = 16 * c2 + tr_row;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS i16x4_t*)(vb + Tl::offset(ra, chn >> 3) + (chn & 4) * 2));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS i16x4_t*)(vb + Tl::offset(ra + 8, chn >> 3) + (chn & 4) * 2));
+        const i16x4_t lohi[2] = {lo, hi};
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lohi), pb, o[t],
+                                                       0, 0, 0);
+      }
+    }
+    // The bf16 chunk and the stage are rewritten only after every read of
+    // this iteration has returned.
+    wait_lds();
+  }
+
+  float* mg = reinterpret_cast<float*>(lds);
+  auto at = [&](int f, int w) -> float& { return mg[(f * kPfWaves + w) * 64 + lane]; };
+  tile_barrier();
+  if (wave != 0) {
+    at(0, wave) = m;
+    at(1, wave) = lsum;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) at(2 + t * 16 + e, wave) = o[t][e];
+  }
+  wait_lds();
+  tile_barrier();
+  if (wave != 0 || !row_ok) return;
+  float mm = m;
+#pragma unroll
+  for (int w = 1; w < kPfWaves; ++w) mm = fmaxf(mm, at(0, w));
+  const float a0 = m == kPfNegInf ? 0.f : fast_exp2(m - mm);
+  lsum *= a0;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[t][e] *= a0;
+#pragma unroll
+  for (int w = 1; w < kPfWaves; ++w) {
+    const float mw = at(0, w);
+    const float aw = mw == kPfNegInf ? 0.f : fast_exp2(mw - mm);
+    lsum += at(1, w) * aw;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[t][e] += at(2 + t * 16 + e, w) * aw;
+  }
+  const float lt = xor32_sum(lsum);
+  const float inv = 1.f / lt;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  const size_t orow = ((size_t)(q0 + tok) * a.h_q + kvh * g + hh) * D;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int chn = t * 32 + 8 * gq + 4 * half;
+      uint2 w;
+      w.x = pack_bf16x2(o[t][4 * gq + 0] * inv, o[t][4 * gq + 1] * inv);
+      w.y = pack_bf16x2(o[t][4 * gq + 2] * inv, o[t][4 * gq + 3] * inv);
+      *reinterpret_cast<uint2*>(&out[orow + chn]) = w;
+    }
+}
+
 static int compute_units_i8() {
   static const int cus = [] {
     int dev = 0, n = 0;
@@ -325,12 +597,18 @@ static int compute_units_i8() {
 template <int D>
 static hipError_t launch_i8_d(const PrefillArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.max_q_len * a.g;
+  PrefillArgs args = a;
+  const int cus = compute_units_i8();
+  if (rows <= 32) {
+    args.longest_first = a.S > 1 && a.S <= kLptMaxSeqs && cus > 0 && (int64_t)a.h_kv * a.S > cus;
+    hipLaunchKernelGGL((prefill_i8_few_rows_kernel<D>), dim3(1, a.h_kv, a.S), dim3(256), 0, stream,
+                       args);
+    return hipGetLastError();
+  }
   const int64_t gx = (rows + kPfRows - 1) / kPfRows;
   const dim3 grid((unsigned)gx, a.h_kv, a.S);
   // Sequence planes longest context first when the grid takes more than one
   // round of the chip (as for the bf16 prefill).
-  PrefillArgs args = a;
-  const int cus = compute_units_i8();
   args.longest_first = a.S > 1 && a.S <= kLptMaxSeqs && cus > 0 && gx * a.h_kv * a.S > cus;
   hipLaunchKernelGGL((prefill_i8_kernel<D>), grid, dim3(256), 0, stream, args);
   return hipGetLastError();

@@ -5,7 +5,8 @@
  * enqueues its kernels on the caller's HIP stream and returns at once.  The
  * library allocates no device memory and its kernel entry points keep no state
  * between calls; they are safe to call from several threads on distinct
- * buffers.  The block manager (pkv_bm_*) is host-only state in a handle the
+ * buffers.  The one exception is paged_decode_attention_noalloc, whose
+ * workspace is a static device array of the library (one per GPU).  The block manager (pkv_bm_*) is host-only state in a handle the
  * caller creates and destroys.
  *
  * Common conventions
@@ -345,7 +346,7 @@ int swap_blocks(const void* const* src_pools, void* const* dst_pools, const int6
  * calls above take.  It is the block pool with per-sequence block tables of
  * the LLM Inference Server page (Optional Stretch Challenges, "Paged KV-Cache
  * Block Allocator"), with blocks shared across requests (Mini inference engine
- * page, section 2), the hash-keyed prefix cache with hit/miss counts whose
+ * page, section 2), the prefix cache with hit/miss counts (hash-keyed there, exact here) whose
  * second request sharing a system prompt skips prefill on it (LLM Inference
  * Server page, Stage 1 "KV-Cache Engine", prefix-cache task; From Scratch page,
  * "Take it further"), a fixed budget that rejects what does not fit so the
@@ -365,9 +366,14 @@ int swap_blocks(const void* const* src_pools, void* const* dst_pools, const int6
  *     blocks with the same preceding tokens, the one sharing the longest run of
  *     leading tokens with the prompt's block (ties: the lowest id).  A whole
  *     16-token match continues with the next block, a shorter one ends the
- *     match; the matched tokens are reported as cached.  The position key is a
- *     64-bit hash chain over the preceding full blocks (the block's own tokens
- *     are compared exactly).
+ *     match; the matched tokens are reported as cached.  The match stops
+ *     before the prompt's last token, which is always left to the prefill (its
+ *     query row gives the next token's logits), so a prompt resubmitted
+ *     exactly hits all but that token.  The preceding tokens are keyed
+ *     exactly, not by a hash: each run of whole 16-token blocks is interned
+ *     once as a node of a trie (parent node, 16 token ids), and a block's key
+ *     is the node of the whole blocks before it, so two different prefixes
+ *     never share a key.
  *   - Writing a token at offset o of a block another sequence also holds
  *     copies it first to a new block (copy on write: one (src, dst) pair).  A
  *     block held alone that holds more than o tokens drops them and is written

@@ -161,22 +161,47 @@ def test_decode_int8_zero_length_and_split_agreement():
     assert torch.equal(bits(a), bits(_decode(w, dev, 1)))
 
 
-@pytest.mark.parametrize("q_mag", [1e-6, 1.0, 3e5])
+@pytest.mark.parametrize("q_mag", [1e-8, 1e-6, 1.0, 3e5])
 def test_decode_int8_query_magnitudes(q_mag):
     """The INT8 decode forms K products in f16 from q scaled by a power of two
-    per piece; queries far outside f16's range (3e5, or 1e-6 where f16 would
-    flush them) must still match the oracle."""
+    per piece; queries far outside f16's range (3e5, or 1e-6 and 1e-8 where f16
+    would flush them) must still match the oracle.  The softmax scale is divided
+    by the magnitude, so the scores keep the spread of |q| ~ 1 instead of
+    collapsing to a one-hot (3e5) or uniform (1e-8) softmax that would hide
+    score errors."""
     rng = np.random.default_rng(4100)
     w = W.build("qmag", rng, dtype="bf16", h_q=16, h_kv=4, d=128,
                 decode_lens=[1, 17, 300, 1000, 2500], free_frac=0.2, poison=True)
     w.dec_q = (w.dec_q.float() * q_mag).to(torch.bfloat16)
+    w.scale = float(np.float32(w.scale / q_mag))  # the kernel takes a float32 scale
     pools = W.int8_pools(w, seed=13, poison=True)
     got, ref = _append(w, pools)
     _check_append_exact(got, ref)
     for splits in (0, 7):
         out = _decode(w, [t.to(DEV) for t in got], splits)
         err = max_err(out, _oracle_decode(w, ref))
+        print(f"|q| ~ {q_mag:g}, splits {splits}: max|err| {err:.3e}")
         assert err <= TOL, f"int8 decode max|err| {err} at |q| ~ {q_mag}"
+
+
+def test_decode_int8_offset_queries():
+    """Queries 50 + N(0, 1): every component has the same sign, so the biased
+    f16 products q . (1152 + c) and the subtracted 1152 * sum(q) nearly cancel;
+    the scores must still match the oracle's.  The scale is divided by 50 to
+    keep the softmax from collapsing to one key."""
+    rng = np.random.default_rng(4101)
+    w = W.build("qoff", rng, dtype="bf16", h_q=16, h_kv=4, d=128,
+                decode_lens=[1, 17, 300, 1000, 2500], free_frac=0.2, poison=True)
+    w.dec_q = (w.dec_q.float() + 50.0).to(torch.bfloat16)
+    w.scale = float(np.float32(w.scale / 50.0))
+    pools = W.int8_pools(w, seed=14, poison=True)
+    got, ref = _append(w, pools)
+    _check_append_exact(got, ref)
+    for splits in (0, 7):
+        out = _decode(w, [t.to(DEV) for t in got], splits)
+        err = max_err(out, _oracle_decode(w, ref))
+        print(f"q = 50 + N(0,1), splits {splits}: max|err| {err:.3e}")
+        assert err <= TOL, f"int8 decode max|err| {err} with offset queries"
 
 
 # ----------------------------------------------------------------------------- prefill

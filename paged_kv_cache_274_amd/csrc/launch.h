@@ -153,6 +153,9 @@ struct PrefillArgs {
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d_h, hipStream_t stream);
+// The bf16 prefill in 8-wave workgroups whose two wave groups alternate matrix
+// and vector phases (for grids of many workgroups).
+hipError_t launch_prefill_pp(const PrefillArgs& a, int d_h, hipStream_t stream);
 // Prefill over an INT8 cache (codes and float32 scales), bf16 queries and output.
 hipError_t launch_prefill_i8(const PrefillArgs& a, int d_h, hipStream_t stream);
 

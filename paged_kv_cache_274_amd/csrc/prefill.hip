@@ -605,6 +605,20 @@ static hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
 #endif
+#ifndef PKV_PF_NO_PP
+  // Many rows per (sequence, KV head) and enough workgroups of 256 rows to
+  // fill the chip: the 8-wave kernel whose wave pairs overlap one wave's MFMAs
+  // with the other's softmax.
+  {
+    const int64_t gx8 = (rows + 255) / 256;
+    const int cus = compute_units();
+    if (rows >= 256 && cus > 0 && gx8 * a.h_kv * a.S >= cus) {
+      PrefillArgs args = a;
+      args.longest_first = a.S > 1 && a.S <= kLptMaxSeqs && gx8 * a.h_kv * a.S > cus;
+      return launch_prefill_pp(args, D, stream);
+    }
+  }
+#endif
   const int64_t gx = (rows + kPfRows - 1) / kPfRows;
   const dim3 grid((unsigned)gx, a.h_kv, a.S);
   // Order the sequence planes longest first when the grid takes more than one

@@ -48,7 +48,10 @@ __device__ __forceinline__ int mfma32_row(int r, int half) { return 8 * (r >> 2)
 // handled explicitly (wait_vm + tile_barrier).  Compiler-generated vmcnt waits
 // stay correct, only stricter, because loads retire in order.
 __device__ __forceinline__ void copy_to_lds(const void* src, const void* lds_dst) {
-  const unsigned lds_addr = (unsigned)(uintptr_t)(const PKV_LDS unsigned char*)lds_dst;
+  // The destination is the same for every lane (m0): make it a scalar even
+  // where the compiler computed it in vector registers.
+  const unsigned lds_addr =
+      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const PKV_LDS unsigned char*)lds_dst);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_addr)
                : "memory");
 }

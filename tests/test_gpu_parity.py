@@ -293,6 +293,41 @@ def test_prefill_grid(d, h_q, h_kv, seqs):
     check_prefill(w, res, kc_ref, vc_ref)
 
 
+# Grids of at least one workgroup of 256 packed rows per compute unit, which
+# take the 8-wave kernel (wave pairs alternating matrix and softmax phases):
+# GQA 1, 2, 4, 7, 8; whole prompts, chunks starting mid-tile, ragged lengths.
+PREFILL_EIGHT_WAVE = [
+    # d, h_q, h_kv, [(context, n_new)], scale (None: 1/sqrt(d))
+    (128, 16, 16, [(1024, 1024), (2000, 700), (900, 900), (1000, 1000)], None),
+    (128, 64, 8, [(300, 300), (1200, 511)], None),
+    (64, 14, 2, [(600, 600)] * 4 + [(1800, 600)] * 4, None),
+    (128, 32, 8, [(3000, 260), (700, 700), (1500, 1000), (2048, 1000)], None),
+    (64, 8, 4, [(513, 513)] * 16, None),
+    (128, 32, 8, [(1100, 1024), (1024, 1024), (640, 640), (2000, 333)], -0.2),
+    (128, 32, 8, [(1100, 1024), (1024, 1024), (640, 640), (2000, 333)], 1.0),
+]
+
+
+@pytest.mark.parametrize("d,h_q,h_kv,seqs,scale", PREFILL_EIGHT_WAVE)
+def test_prefill_eight_wave_grid(d, h_q, h_kv, seqs, scale):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows = max(n for _, n in seqs) * (h_q // h_kv)
+    assert rows >= 256 and -(-rows // 256) * h_kv * len(seqs) >= cus, "not the 8-wave launch"
+    rng = np.random.default_rng(2200 + d + h_q + h_kv + len(seqs))
+    w = W.build("pp", rng, dtype="bf16", h_q=h_q, h_kv=h_kv, d=d, prefill=seqs,
+                free_frac=0.1, poison=True, scale=scale)
+    res = run(w, DEV, do_decode=False)
+    kc_ref, vc_ref = check_append(w, res)
+    # The bf16 output rounding is relative (half an ulp, 2^-9 |o|): with scale
+    # 1.0 the softmax is nearly one-hot and outputs reach |o| ~ 4.8, where half
+    # an ulp is 1/64, so the bound is taken relative to max(1, |o|).
+    ref = pins.oracle_prefill(w, kc_ref, vc_ref)
+    got = res.prefill.double().numpy()
+    err = float((np.abs(got - ref) / np.maximum(1.0, np.abs(ref))).max())
+    print(f"eight-wave prefill {d}/{h_q}/{h_kv} scale {scale}: max|err|/max(1,|ref|) {err:.3e}")
+    assert err <= 2e-2
+
+
 @pytest.mark.parametrize("d,h_q,h_kv,seqs", [
     (128, 32, 8, [(512, 512)] * 16),
     (64, 14, 2, [(512, 512)] * 40),
@@ -300,7 +335,7 @@ def test_prefill_grid(d, h_q, h_kv, seqs):
 ])
 def test_prefill_full_prompts_many_rounds(d, h_q, h_kv, seqs):
     """Whole and chunked prompts on grids of several rounds of the chip (the
-    software-pipelined key walk with four tile buffers, longest context first)."""
+    8-wave kernel, sequence planes longest context first)."""
     rng = np.random.default_rng(2100 + d + len(seqs))
     w = W.build("rb2", rng, dtype="bf16", h_q=h_q, h_kv=h_kv, d=d, prefill=seqs,
                 free_frac=0.1, poison=True)

@@ -56,6 +56,24 @@ __device__ __forceinline__ void copy_to_lds(const void* src, const void* lds_dst
                : "memory");
 }
 
+// The same copy with the source given as a wave-uniform base (a scalar
+// register pair) plus this lane's 32-bit byte offset, so that no 64-bit
+// vector address arithmetic is needed per copy.
+__device__ __forceinline__ void copy_to_lds_off(const void* base, uint32_t off,
+                                                const void* lds_dst) {
+  const unsigned lds_addr =
+      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const PKV_LDS unsigned char*)lds_dst);
+  // readfirstlane returns int: each half goes through uint32_t so that the
+  // low word is not sign-extended into the high one.
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)b);
+  const uint64_t sb = ((uint64_t)hi << 32) | lo;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb),
+               "s"(lds_addr)
+               : "memory");
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vm() {

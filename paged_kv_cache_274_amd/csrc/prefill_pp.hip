@@ -110,9 +110,9 @@ __global__ __launch_bounds__(64 * kPpWaves) void prefill_pp_kernel(PrefillArgs a
   // stays off the walk.
   auto entry = [&](int kt) -> int {
     const int bi = min(kt * (kPfTile / kBlock) + (wave >> 1), last_tok >> 4);
-    const int blk = constant_view(trow)[bi];
-    return (blk >= 0 && blk < a.n_blocks) ? blk : 0;
+    return constant_view(trow)[bi];
   };
+  auto clamp_entry = [&](int blk) { return (blk >= 0 && blk < a.n_blocks) ? blk : 0; };
   // Lane part of each copy's source (row rb of the block, the chunk that lands
   // at this lane's LDS position) for blocks wholly inside the context.
   uint32_t src_off[kCopies], chunk_off[kCopies];
@@ -134,15 +134,15 @@ __global__ __launch_bounds__(64 * kPpWaves) void prefill_pp_kernel(PrefillArgs a
     if (bi * kBlock + kBlock <= L) {
 #pragma unroll
       for (int i = 0; i < kCopies; ++i)
-        copy_to_lds(src + src_off[i],
-                    slot + (kRowsPerWave * wave + i * Tl::kRowsPerCopy) * Tl::kRowBytes);
+        copy_to_lds_off(src, src_off[i],
+                        slot + (kRowsPerWave * wave + i * Tl::kRowsPerCopy) * Tl::kRowBytes);
     } else {
 #pragma unroll
       for (int i = 0; i < kCopies; ++i) {
         const int rb = 8 * (wave & 1) + i * Tl::kRowsPerCopy + lane / Tl::kChunks;
         const int rbe = bi * kBlock + rb < L ? rb : (last_tok & (kBlock - 1));
-        copy_to_lds(src + rbe * Tl::kRowBytes + chunk_off[i],
-                    slot + (kRowsPerWave * wave + i * Tl::kRowsPerCopy) * Tl::kRowBytes);
+        copy_to_lds_off(src, rbe * Tl::kRowBytes + chunk_off[i],
+                        slot + (kRowsPerWave * wave + i * Tl::kRowsPerCopy) * Tl::kRowBytes);
       }
     }
   };
@@ -249,11 +249,20 @@ __global__ __launch_bounds__(64 * kPpWaves) void prefill_pp_kernel(PrefillArgs a
         for (int i = 0; i < 16; ++i)
           if (32 * h2 + mfma32_row(i, 0) > lim) st[h2][i] = kPfNegInf;
     }
-    float tmax = kPfNegInf;
+    // Row maximum as a tree of three-input maxima (depth 4, not a chain of 16).
+    float t1[11];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, st[h2][i]);
+    for (int j = 0; j < 10; ++j) {
+      const int e = 3 * j;
+      t1[j] = fmaxf(fmaxf(st[e >> 4][e & 15], st[(e + 1) >> 4][(e + 1) & 15]),
+                    st[(e + 2) >> 4][(e + 2) & 15]);
+    }
+    t1[10] = fmaxf(st[1][14], st[1][15]);
+    const float t2a = fmaxf(fmaxf(t1[0], t1[1]), t1[2]);
+    const float t2b = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
+    const float t2c = fmaxf(fmaxf(t1[6], t1[7]), t1[8]);
+    const float t2d = fmaxf(t1[9], t1[10]);
+    float tmax = fmaxf(fmaxf(t2a, t2b), fmaxf(t2c, t2d));
     tmax = xor32_max(tmax) * csc;
     if (__any(tmax > m + kPfSlack)) {
       const float mn = tmax > m + kPfSlack ? tmax : m;
@@ -266,31 +275,33 @@ __global__ __launch_bounds__(64 * kPpWaves) void prefill_pp_kernel(PrefillArgs a
         for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
     }
     const float mn = m == kPfNegInf ? 0.f : m;
-    float ps = 0.f;
+    // The row sum adds the bf16 weights the P.V products use, two per v_dot2
+    // against (1, 1), in two independent chains.
+    const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       // Weights of keys 16c .. 16c + 15 in the P^T operand order (see
       // prefill_bf16_kernel): accumulators 8 * (c % 2) .. + 7 of half-tile c / 2.
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = fast_exp2(fmaf(st[c >> 1][8 * (c & 1) + e], csc, -mn));
-        ps += p[e];
-      }
-      uint4 pw;
-      pw.x = pack_bf16x2(p[0], p[1]);
-      pw.y = pack_bf16x2(p[2], p[3]);
-      pw.z = pack_bf16x2(p[4], p[5]);
-      pw.w = pack_bf16x2(p[6], p[7]);
-      pb[c] = __builtin_bit_cast(bf16x8_t, pw);
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(st[c >> 1][8 * (c & 1) + e], csc, -mn));
+      uint32_t pw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[0]), ones, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[1]), ones, ps1, false);
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[2]), ones, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[3]), ones, ps1, false);
+      pb[c] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
     }
-    lsum += ps;
+    lsum += ps0 + ps1;
   };
 
   // Prologue: keys of tiles 0 and 1, values of tile 0, then Q; one wait for all.
-  const int e0 = entry(0);
-  int e_v = entry(1);  // entry of the tile whose values are issued next
-  int e_k = entry(2);  // entry of the tile whose keys are issued next
+  const int e0 = clamp_entry(entry(0));
+  int e_v = clamp_entry(entry(1));  // entry of the tile whose values are issued next
+  int e_k = clamp_entry(entry(2));  // entry of the tile whose keys are issued next
   issue(kc, kslot(0), 0, e0);
   if (n_tiles > 1) issue(kc, kslot(1), 1, e_v);
   issue(vc, vslot(0), 0, e0);
@@ -324,9 +335,19 @@ __global__ __launch_bounds__(64 * kPpWaves) void prefill_pp_kernel(PrefillArgs a
     if (t + 2 < n_tiles) issue(kc, kslot(t + 2), t + 2, e_k);
     if (t + 1 < n_tiles) issue(vc, vslot(t + 1), t + 1, e_v);
   };
-  auto next_entries = [&](int t) {  // after interval 2t's copies: tile t + 3's entry
+  // After interval 2t's copies: tile t + 3's entry, loaded at the start of a
+  // vector phase and clamped (the first use of the loaded value, where the
+  // wave waits for it) only at its end, behind a scheduling barrier, so the
+  // load's latency hides under the softmax and no scalar load is in flight
+  // when the next matrix phase waits on its LDS reads.
+  int e_raw = 0;
+  auto next_entries = [&](int t) {
     e_v = e_k;
-    e_k = entry(t + 3);
+    e_raw = entry(t + 3);
+  };
+  auto entries_landed = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    e_k = clamp_entry(e_raw);
   };
   auto wait_for_interval = [&](int t) {  // the wait at the end of interval 2t + 1
     const bool k = t + 2 < n_tiles, v = t + 1 < n_tiles;
@@ -350,6 +371,7 @@ __global__ __launch_bounds__(64 * kPpWaves) void prefill_pp_kernel(PrefillArgs a
       tile_barrier();
       next_entries(t);
       if constexpr (decltype(KS_)::value) vector_phase(t);
+      entries_landed();
       wait_for_interval(t);
       tile_barrier();
     };
@@ -365,6 +387,7 @@ __global__ __launch_bounds__(64 * kPpWaves) void prefill_pp_kernel(PrefillArgs a
     // Intervals 2t + 1 (matrix phase) and 2t + 2 (vector phase).
     issue_for_interval(0);
     next_entries(0);
+    entries_landed();
     tile_barrier();
     auto period = [&](int t, auto KS_, auto KPV_) {
       matrix_phase(t, KS_, KPV_);
@@ -374,6 +397,7 @@ __global__ __launch_bounds__(64 * kPpWaves) void prefill_pp_kernel(PrefillArgs a
       issue_for_interval(t + 1);
       next_entries(t + 1);
       if constexpr (decltype(KS_)::value) vector_phase(t);
+      entries_landed();
       tile_barrier();
     };
     int t = 0;

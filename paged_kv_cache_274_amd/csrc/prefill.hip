@@ -54,6 +54,22 @@ __global__ __launch_bounds__(256 * KS) void prefill_bf16_kernel(PrefillArgs a) {
   const int s = a.longest_first ? longest_first_sequence(a, blockIdx.z) : (int)blockIdx.z;
   const int kvh = blockIdx.y;
   const int g = a.g;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // row wave in the group
+  const int grp_id = __builtin_amdgcn_readfirstlane(tid >> 8);       // key-split group
+  // Block-table entries of this wave's blocks of tile kt.  The index stays
+  // inside the table row without waiting for the context length: entries past
+  // the context may hold anything, so the block id is clamped into the pool
+  // when used, and those rows are masked (K) or zeroed (V).  The first two
+  // tiles' entries are loaded together with the sequence's offsets, one
+  // memory round trip before they would be otherwise.
+  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  auto entry = [&](int kt) -> int {
+    return constant_view(trow)[min(kt * (kPfTile / kBlock) + wave, a.max_blocks_per_seq - 1)];
+  };
+  int e_a = entry(grp_id);
+  const int e_b = entry(grp_id + KS);
   const int q0 = a.cu_seqlens_q[s];
   const int n = a.cu_seqlens_q[s + 1] - q0;
   int L = a.context_lens[s];
@@ -62,10 +78,6 @@ __global__ __launch_bounds__(256 * KS) void prefill_bf16_kernel(PrefillArgs a) {
   const int r0 = bx * kPfRows;
   if (n <= 0 || n > L || r0 >= rows || q0 < 0 || q0 + n > a.T_q) return;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // row wave in the group
-  const int grp_id = __builtin_amdgcn_readfirstlane(tid >> 8);       // key-split group
   const int col = lane & 31;
   const int half = lane >> 5;
   const int first = L - n;  // position of query 0
@@ -102,7 +114,6 @@ __global__ __launch_bounds__(256 * KS) void prefill_bf16_kernel(PrefillArgs a) {
 
   const unsigned char* kc = reinterpret_cast<const unsigned char*>(a.k_cache);
   const unsigned char* vc = reinterpret_cast<const unsigned char*>(a.v_cache);
-  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   const size_t head_bytes = (size_t)kBlock * Tl::kRowBytes;
 
   // The group's i-th tile lives in its buffer i % 3.
@@ -111,15 +122,11 @@ __global__ __launch_bounds__(256 * KS) void prefill_bf16_kernel(PrefillArgs a) {
   };
   auto buffer = [&](auto B) -> unsigned char* { return buffer_of(grp_id, B); };
 
-  // Copies block (4 * kt + wave) of tile kt, K and V, into its buffer.  Lane l
+  // Copies this wave's block of a tile (block id blk, block 4 * kt + wave of
+  // the table row), K and V, into buffer B.  Lane l
   // of copy i fills LDS row 16 * wave + i * kRowsPerCopy + l / kChunks at chunk
   // position l % kChunks, i.e. logical chunk (l % kChunks) ^ swz(row).
-  auto issue_tile = [&](auto B, int kt) {
-    // The entry index stays inside the table row but does not wait for the
-    // context length: entries past the context may hold anything, so the block
-    // id is clamped into the pool, and those rows are masked (K) or zeroed (V).
-    const int bi = min(kt * (kPfTile / kBlock) + wave, a.max_blocks_per_seq - 1);
-    int blk = constant_view(trow)[bi];
+  auto issue_tile = [&](auto B, int blk) {
     blk = (blk >= 0 && blk < a.n_blocks) ? blk : 0;
     const size_t gbase = ((size_t)blk * a.h_kv + kvh) * head_bytes;
     unsigned char* buf = buffer(B);
@@ -260,13 +267,19 @@ __global__ __launch_bounds__(256 * KS) void prefill_bf16_kernel(PrefillArgs a) {
       tile_barrier();
     }
     if (mine && kt + 2 * KS < n_tiles)
-      issue_tile(std::integral_constant<int, (decltype(B)::value + 2) % 3>{}, kt + 2 * KS);
+      issue_tile(std::integral_constant<int, (decltype(B)::value + 2) % 3>{}, e_a);
     if (mine && wave_live && kt * kPfTile <= wave_pos_hi) attend_tile(B, kt);
+    // The entry of the tile the next step issues, loaded after this tile's LDS
+    // reads (a scalar load in flight makes every LDS wait a full wait) and
+    // used one barrier later.
+    __builtin_amdgcn_sched_barrier(0);
+    e_a = entry(kt + 3 * KS);
     return true;
   };
 
-  if (grp_id < n_tiles) issue_tile(std::integral_constant<int, 0>{}, grp_id);
-  if (grp_id + KS < n_tiles) issue_tile(std::integral_constant<int, 1>{}, grp_id + KS);
+  if (grp_id < n_tiles) issue_tile(std::integral_constant<int, 0>{}, e_a);
+  if (grp_id + KS < n_tiles) issue_tile(std::integral_constant<int, 1>{}, e_b);
+  e_a = entry(grp_id + 2 * KS);
 
   // Q^T operand (B of S^T = K Q^T): lane (col, half) holds channels
   // 16c + 8*half .. +8 of its row; rows past the end are zero.  The wait that

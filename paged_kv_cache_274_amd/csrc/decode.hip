@@ -448,6 +448,159 @@ __device__ __forceinline__ void attend_block(const BlockOf<T, D>& r,
   }
 }
 
+// INT8 cache, d_h = 128, chunks of 4 heads: a row of 16 lanes shares 4 tokens
+// (one per pass) and forms 16 partial scores per lane, one per (pass, head).
+// attend_block sums each across the row (4 DPP steps for each of the 16) and
+// then every lane repeats the same scaling, exponential and sum for all 16.
+// Here the row's partial scores are reduce-scattered instead, so that lane i
+// of the row ends with the full score of one (pass, head) pair: 45
+// instructions for the sum, then one scale, one exponential and one sum term
+// per lane; the P.V weights return to every lane of the row as 8 packed bf16
+// pairs by row broadcasts.  The running maximum m[j] stays replicated across
+// the row; m_sel is this lane's head's copy, and l_slot the lane's share of
+// its head's sum, combined into l[j] at the end of a piece (rs_finish_sum).
+template <typename T, int D, int GC>
+constexpr bool kScatterScores = std::is_same<T, i8_t>::value && D == 128 && GC == 4;
+
+// Index of the (pass ps, head j) score in the scatter order; lane i of a row
+// ends with index i, so pass 2i and 2i + 1 of a head (the two weights one P.V
+// word pairs) sit one lane apart.
+__device__ constexpr int rs_index(int ps, int j) { return 8 * (ps >> 1) + 2 * j + (ps & 1); }
+
+// One level of the reduce-scatter: v[0 .. 2n-1] becomes v[0 .. n-1], the half
+// this lane keeps (the upper one if hi) summed with the partner's copy of it;
+// the partner (DPP control CTRL) keeps the other half.
+template <int CTRL, int N>
+__device__ __forceinline__ void rs_level(float (&v)[16], bool hi) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const float keep = hi ? v[k + N] : v[k];
+    const float send = hi ? v[k] : v[k + N];
+    v[k] = keep + dpp<CTRL>(send);
+  }
+}
+
+// The entry of four values that belongs to this lane's pass (2 * b3 + b0),
+// chosen by selects on values: each passes through an empty asm first, so
+// that the selects are not folded into one dynamically indexed read of the
+// block's registers, which would move the whole block to scratch memory.
+__device__ __forceinline__ float pick_pass(const float (&x)[4], bool b3, bool b0) {
+  float x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];
+  asm("" : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3));
+  return b3 ? (b0 ? x3 : x2) : (b0 ? x1 : x0);
+}
+
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xf, 0xf, false));
+}
+template <int N>
+__device__ __forceinline__ uint32_t row_bcast_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + N, 0xf, 0xf, false);
+}
+
+template <int D, int GC, bool MASK>
+__device__ __forceinline__ void attend_block_rs(const BlockOf<i8_t, D>& r,
+                                                const QRegs<GC, DecodeShape<i8_t, D>::kVPL>& q,
+                                                float (&m)[GC], float& m_sel, float& l_slot,
+                                                float (&acc)[GC][DecodeShape<i8_t, D>::kEPL],
+                                                int slot, int valid, int i16) {
+  constexpr int NP = DecodeShape<i8_t, D>::kPasses;
+  static_assert(NP == 4 && GC == 4, "16 scores over 16 lanes");
+  float v[16];
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps)
+#pragma unroll
+    for (int j = 0; j < GC; ++j) v[rs_index(ps, j)] = q.bias[j];
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int ps = 0; ps < NP; ++ps) {
+      const uint32_t kw = __builtin_amdgcn_perm(
+          0x64646464u, ((w < 2) ? r.k[ps].x : r.k[ps].y) ^ 0x80808080u,
+          (w & 1) ? 0x04030402u : 0x04010400u);
+#pragma unroll
+      for (int j = 0; j < GC; ++j)
+        v[rs_index(ps, j)] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, kw),
+                                                    __builtin_bit_cast(f16x2_t, q.w[j][w]),
+                                                    v[rs_index(ps, j)], false);
+    }
+  const bool b3 = i16 & 8, b2 = i16 & 4, b1 = i16 & 2, b0 = i16 & 1;
+  rs_level<kDppRowMirror, 8>(v, b3);
+  rs_level<kDppRowHalfMirror, 4>(v, b2);
+  rs_level<kDppXor2, 2>(v, b1);
+  rs_level<kDppXor1, 1>(v, b0);
+  // This lane's score: pass ps = 2 * b3 + b0 (token slot * NP + ps), head
+  // (i16 >> 1) & 3.
+  const int ps = 2 * b3 + b0;
+  const float ks = pick_pass(r.ks, b3, b0);
+  float x = v[0] * (ks * q.sfac);
+  const bool ok = !MASK || token_of<i8_t, D>(ps, slot) < valid;
+  if (MASK) x = ok ? x : kNegInf;
+  if (__any(x > m_sel + kRescaleSlack)) {
+    // The row's maximum of this lane's head over the 4 passes (lanes i, i ^ 1,
+    // i ^ 8, i ^ 9), the lazy rescale of attend_block, and the new maxima and
+    // factors sent to every lane of the row for the accumulators.
+    float mx = fmaxf(x, dpp<kDppXor1>(x));
+    mx = fmaxf(mx, dpp<kDppRowRor8>(mx));
+    const float mn = mx > m_sel + kRescaleSlack ? mx : m_sel;
+    const float alpha = mn == m_sel ? 1.f : fast_exp2(m_sel - mn);
+    m_sel = mn;
+    l_slot *= alpha;
+    const float al[4] = {row_bcast<0>(alpha), row_bcast<2>(alpha), row_bcast<4>(alpha),
+                         row_bcast<6>(alpha)};
+    m[0] = row_bcast<0>(mn);
+    m[1] = row_bcast<2>(mn);
+    m[2] = row_bcast<4>(mn);
+    m[3] = row_bcast<6>(mn);
+#pragma unroll
+    for (int j = 0; j < GC; ++j)
+#pragma unroll
+      for (int e = 0; e < DecodeShape<i8_t, D>::kEPL; ++e) acc[j][e] *= al[j];
+  }
+  float p = fast_exp2(x - m_sel);
+  if (MASK) p = ok ? p : 0.f;
+  l_slot += p;
+  // The weight carries the token's V scale (a masked token's weight is zero
+  // whatever its scale slot holds), rounded to bf16 once in the pair with the
+  // next pass's weight; even lanes hold the pairs.
+  const float vs = pick_pass(r.vs, b3, b0);
+  float w = p * vs;
+  if (MASK) w = ok ? w : 0.f;
+  const uint32_t pk = pack_bf16x2(w, dpp<kDppXor1>(w));
+  uint32_t pp[2][GC];
+  pp[0][0] = row_bcast_u<0>(pk);
+  pp[0][1] = row_bcast_u<2>(pk);
+  pp[0][2] = row_bcast_u<4>(pk);
+  pp[0][3] = row_bcast_u<6>(pk);
+  pp[1][0] = row_bcast_u<8>(pk);
+  pp[1][1] = row_bcast_u<10>(pk);
+  pp[1][2] = row_bcast_u<12>(pk);
+  pp[1][3] = row_bcast_u<14>(pk);
+#pragma unroll
+  for (int pr = 0; pr < NP / 2; ++pr)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t xv = i8_pair_bf16(i8_code(r.v[2 * pr], c), i8_code(r.v[2 * pr + 1], c));
+#pragma unroll
+      for (int j = 0; j < GC; ++j)
+        acc[j][c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp[pr][j]),
+                                                    __builtin_bit_cast(bf16x2_t, xv), acc[j][c],
+                                                    false);
+    }
+}
+
+// The row's sums per head from the lanes' shares: l[j] on every lane of the row.
+template <int GC>
+__device__ __forceinline__ void rs_finish_sum(float l_slot, float (&l)[GC]) {
+  float t = l_slot + dpp<kDppXor1>(l_slot);
+  t += dpp<kDppRowRor8>(t);
+  l[0] = row_bcast<0>(t);
+  l[1] = row_bcast<2>(t);
+  l[2] = row_bcast<4>(t);
+  l[3] = row_bcast<6>(t);
+}
+
 template <typename T>
 __device__ __forceinline__ void store_elem(T* out, size_t i, float x) {
   if constexpr (std::is_same<T, float>::value)
@@ -753,7 +906,10 @@ struct RangeStream {
     }
 
     float m[GC], l[GC], acc[GC][EPL];
+    float m_sel = kNegInf, l_slot = 0.f;  // reduce-scattered scores only
     auto reset = [&]() {
+      m_sel = kNegInf;
+      l_slot = 0.f;
 #pragma unroll
       for (int j = 0; j < GC; ++j) {
         m[j] = kNegInf;
@@ -775,7 +931,10 @@ struct RangeStream {
     auto step_in = [&](BlockOf<T, D>& X, BlockOf<T, D>& Y, int& E) {
       load_block<T, D>(Y, a, block_head(E, cc.kvh), slot_id, sub);
       E = table_entry(cc, min(t + 3, cur.j1 - 1));
-      attend_block<T, D, GC, false>(X, q, m, l, acc, a.scale_log2, slot_id, kBlock);
+      if constexpr (kScatterScores<T, D, GC>)
+        attend_block_rs<D, GC, false>(X, q, m, m_sel, l_slot, acc, slot_id, kBlock, sub);
+      else
+        attend_block<T, D, GC, false>(X, q, m, l, acc, a.scale_log2, slot_id, kBlock);
       ++t;
       if (++walked == prio_until) __builtin_amdgcn_s_setprio(0);
     };
@@ -787,10 +946,17 @@ struct RangeStream {
         load_block<T, D>(Y, a, block_head(nxt_blk0, nc.kvh), slot_id, sub);
       }
       const int valid = cc.L - t * kBlock;
-      if (valid >= kBlock)
-        attend_block<T, D, GC, false>(X, q, m, l, acc, a.scale_log2, slot_id, kBlock);
-      else
-        attend_block<T, D, GC, true>(X, q, m, l, acc, a.scale_log2, slot_id, valid);
+      if constexpr (kScatterScores<T, D, GC>) {
+        if (valid >= kBlock)
+          attend_block_rs<D, GC, false>(X, q, m, m_sel, l_slot, acc, slot_id, kBlock, sub);
+        else
+          attend_block_rs<D, GC, true>(X, q, m, m_sel, l_slot, acc, slot_id, valid, sub);
+      } else {
+        if (valid >= kBlock)
+          attend_block<T, D, GC, false>(X, q, m, l, acc, a.scale_log2, slot_id, kBlock);
+        else
+          attend_block<T, D, GC, true>(X, q, m, l, acc, a.scale_log2, slot_id, valid);
+      }
     };
 
     if constexpr (kF16Codes<T, GC>) q_for_codes(q, a.scale_log2);
@@ -826,6 +992,7 @@ struct RangeStream {
           in_b = true;
         }
       }
+      if constexpr (kScatterScores<T, D, GC>) rs_finish_sum<GC>(l_slot, l);
       epilogue(a, line, W, cur, cc, lane, m, l, acc);
       if (!nxt.valid) break;
       cur = nxt;

@@ -460,7 +460,8 @@ __device__ __forceinline__ void attend_block(const BlockOf<T, D>& r,
 // the row; m_sel is this lane's head's copy, and l_slot the lane's share of
 // its head's sum, combined into l[j] at the end of a piece (rs_finish_sum).
 template <typename T, int D, int GC>
-constexpr bool kScatterScores = std::is_same<T, i8_t>::value && D == 128 && GC == 4;
+constexpr bool kScatterScores =
+    (std::is_same<T, i8_t>::value || std::is_same<T, bf16_t>::value) && D == 128 && GC == 4;
 
 // Index of the (pass ps, head j) score in the scatter order; lane i of a row
 // ends with index i, so pass 2i and 2i + 1 of a head (the two weights one P.V
@@ -499,43 +500,56 @@ __device__ __forceinline__ uint32_t row_bcast_u(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + N, 0xf, 0xf, false);
 }
 
-template <int D, int GC, bool MASK>
-__device__ __forceinline__ void attend_block_rs(const BlockOf<i8_t, D>& r,
-                                                const QRegs<GC, DecodeShape<i8_t, D>::kVPL>& q,
+template <typename T, int D, int GC, bool MASK>
+__device__ __forceinline__ void attend_block_rs(const BlockOf<T, D>& r,
+                                                const QRegs<GC, DecodeShape<T, D>::kVPL>& q,
                                                 float (&m)[GC], float& m_sel, float& l_slot,
-                                                float (&acc)[GC][DecodeShape<i8_t, D>::kEPL],
-                                                int slot, int valid, int i16) {
-  constexpr int NP = DecodeShape<i8_t, D>::kPasses;
-  static_assert(NP == 4 && GC == 4, "16 scores over 16 lanes");
+                                                float (&acc)[GC][DecodeShape<T, D>::kEPL],
+                                                float scale_log2, int slot, int valid, int i16) {
+  constexpr int NP = DecodeShape<T, D>::kPasses;
+  constexpr bool kI8 = std::is_same<T, i8_t>::value;
+  static_assert(NP == 4 && GC == 4 && DecodeShape<T, D>::kVPL == 1, "16 scores over 16 lanes");
   float v[16];
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps)
 #pragma unroll
-    for (int j = 0; j < GC; ++j) v[rs_index(ps, j)] = q.bias[j];
+    for (int j = 0; j < GC; ++j) v[rs_index(ps, j)] = kI8 ? q.bias[j] : 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w)
 #pragma unroll
     for (int ps = 0; ps < NP; ++ps) {
-      const uint32_t kw = __builtin_amdgcn_perm(
-          0x64646464u, ((w < 2) ? r.k[ps].x : r.k[ps].y) ^ 0x80808080u,
-          (w & 1) ? 0x04030402u : 0x04010400u);
+      if constexpr (kI8) {
+        const uint32_t kw = __builtin_amdgcn_perm(
+            0x64646464u, ((w < 2) ? r.k[ps].x : r.k[ps].y) ^ 0x80808080u,
+            (w & 1) ? 0x04030402u : 0x04010400u);
 #pragma unroll
-      for (int j = 0; j < GC; ++j)
-        v[rs_index(ps, j)] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, kw),
-                                                    __builtin_bit_cast(f16x2_t, q.w[j][w]),
-                                                    v[rs_index(ps, j)], false);
+        for (int j = 0; j < GC; ++j)
+          v[rs_index(ps, j)] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, kw),
+                                                      __builtin_bit_cast(f16x2_t, q.w[j][w]),
+                                                      v[rs_index(ps, j)], false);
+      } else {
+        const uint32_t kw = dw(r.k[ps][0], w);
+#pragma unroll
+        for (int j = 0; j < GC; ++j)
+          v[rs_index(ps, j)] = __builtin_amdgcn_fdot2_f32_bf16(
+              __builtin_bit_cast(bf16x2_t, kw), __builtin_bit_cast(bf16x2_t, q.w[j][w]),
+              v[rs_index(ps, j)], false);
+      }
     }
   const bool b3 = i16 & 8, b2 = i16 & 4, b1 = i16 & 2, b0 = i16 & 1;
   rs_level<kDppRowMirror, 8>(v, b3);
   rs_level<kDppRowHalfMirror, 4>(v, b2);
   rs_level<kDppXor2, 2>(v, b1);
   rs_level<kDppXor1, 1>(v, b0);
-  // This lane's score: pass ps = 2 * b3 + b0 (token slot * NP + ps), head
-  // (i16 >> 1) & 3.
+  // This lane's score: pass ps = 2 * b3 + b0, head (i16 >> 1) & 3.  An INT8
+  // score takes its token's K scale and the query's power of two.
   const int ps = 2 * b3 + b0;
-  const float ks = pick_pass(r.ks, b3, b0);
-  float x = v[0] * (ks * q.sfac);
-  const bool ok = !MASK || token_of<i8_t, D>(ps, slot) < valid;
+  float x;
+  if constexpr (kI8)
+    x = v[0] * (pick_pass(r.ks, b3, b0) * q.sfac);
+  else
+    x = v[0] * scale_log2;
+  const bool ok = !MASK || token_of<T, D>(ps, slot) < valid;
   if (MASK) x = ok ? x : kNegInf;
   if (__any(x > m_sel + kRescaleSlack)) {
     // The row's maximum of this lane's head over the 4 passes (lanes i, i ^ 1,
@@ -556,16 +570,16 @@ __device__ __forceinline__ void attend_block_rs(const BlockOf<i8_t, D>& r,
 #pragma unroll
     for (int j = 0; j < GC; ++j)
 #pragma unroll
-      for (int e = 0; e < DecodeShape<i8_t, D>::kEPL; ++e) acc[j][e] *= al[j];
+      for (int e = 0; e < DecodeShape<T, D>::kEPL; ++e) acc[j][e] *= al[j];
   }
   float p = fast_exp2(x - m_sel);
   if (MASK) p = ok ? p : 0.f;
   l_slot += p;
-  // The weight carries the token's V scale (a masked token's weight is zero
-  // whatever its scale slot holds), rounded to bf16 once in the pair with the
-  // next pass's weight; even lanes hold the pairs.
-  const float vs = pick_pass(r.vs, b3, b0);
-  float w = p * vs;
+  // An INT8 weight carries the token's V scale (a masked token's weight is
+  // zero whatever its scale slot holds); the weight is rounded to bf16 once,
+  // in the pair with the next pass's weight; even lanes hold the pairs.
+  float w = p;
+  if constexpr (kI8) w = p * pick_pass(r.vs, b3, b0);
   if (MASK) w = ok ? w : 0.f;
   const uint32_t pk = pack_bf16x2(w, dpp<kDppXor1>(w));
   uint32_t pp[2][GC];
@@ -577,17 +591,48 @@ __device__ __forceinline__ void attend_block_rs(const BlockOf<i8_t, D>& r,
   pp[1][1] = row_bcast_u<10>(pk);
   pp[1][2] = row_bcast_u<12>(pk);
   pp[1][3] = row_bcast_u<14>(pk);
+  if constexpr (kI8) {
 #pragma unroll
-  for (int pr = 0; pr < NP / 2; ++pr)
+    for (int pr = 0; pr < NP / 2; ++pr)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t xv = i8_pair_bf16(i8_code(r.v[2 * pr], c), i8_code(r.v[2 * pr + 1], c));
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t xv = i8_pair_bf16(i8_code(r.v[2 * pr], c), i8_code(r.v[2 * pr + 1], c));
 #pragma unroll
-      for (int j = 0; j < GC; ++j)
-        acc[j][c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp[pr][j]),
-                                                    __builtin_bit_cast(bf16x2_t, xv), acc[j][c],
-                                                    false);
-    }
+        for (int j = 0; j < GC; ++j)
+          acc[j][c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp[pr][j]),
+                                                      __builtin_bit_cast(bf16x2_t, xv), acc[j][c],
+                                                      false);
+      }
+  } else {
+    // Tokens of passes 2pr and 2pr + 1 paired per channel, as in attend_block;
+    // V rows past the context are zeroed, since a zero weight times a NaN is NaN.
+    const bool ok0 = !MASK || token_of<T, D>(0, slot) < valid;
+    const bool ok1 = !MASK || token_of<T, D>(1, slot) < valid;
+    const bool ok2 = !MASK || token_of<T, D>(2, slot) < valid;
+    const bool ok3 = !MASK || token_of<T, D>(3, slot) < valid;
+    const bool okp[4] = {ok0, ok1, ok2, ok3};
+#pragma unroll
+    for (int pr = 0; pr < NP / 2; ++pr)
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        uint32_t x0 = dw(r.v[2 * pr][0], w4), x1 = dw(r.v[2 * pr + 1][0], w4);
+        if (MASK) {
+          x0 = okp[2 * pr] ? x0 : 0u;
+          x1 = okp[2 * pr + 1] ? x1 : 0u;
+        }
+        const uint32_t lo = __builtin_amdgcn_perm(x1, x0, 0x05040100u);  // channel 2w
+        const uint32_t hi = __builtin_amdgcn_perm(x1, x0, 0x07060302u);  // channel 2w+1
+#pragma unroll
+        for (int j = 0; j < GC; ++j) {
+          acc[j][2 * w4] = __builtin_amdgcn_fdot2_f32_bf16(
+              __builtin_bit_cast(bf16x2_t, pp[pr][j]), __builtin_bit_cast(bf16x2_t, lo),
+              acc[j][2 * w4], false);
+          acc[j][2 * w4 + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+              __builtin_bit_cast(bf16x2_t, pp[pr][j]), __builtin_bit_cast(bf16x2_t, hi),
+              acc[j][2 * w4 + 1], false);
+        }
+      }
+  }
 }
 
 // The row's sums per head from the lanes' shares: l[j] on every lane of the row.
@@ -932,7 +977,8 @@ struct RangeStream {
       load_block<T, D>(Y, a, block_head(E, cc.kvh), slot_id, sub);
       E = table_entry(cc, min(t + 3, cur.j1 - 1));
       if constexpr (kScatterScores<T, D, GC>)
-        attend_block_rs<D, GC, false>(X, q, m, m_sel, l_slot, acc, slot_id, kBlock, sub);
+        attend_block_rs<T, D, GC, false>(X, q, m, m_sel, l_slot, acc, a.scale_log2, slot_id, kBlock,
+                                         sub);
       else
         attend_block<T, D, GC, false>(X, q, m, l, acc, a.scale_log2, slot_id, kBlock);
       ++t;
@@ -948,9 +994,11 @@ struct RangeStream {
       const int valid = cc.L - t * kBlock;
       if constexpr (kScatterScores<T, D, GC>) {
         if (valid >= kBlock)
-          attend_block_rs<D, GC, false>(X, q, m, m_sel, l_slot, acc, slot_id, kBlock, sub);
+          attend_block_rs<T, D, GC, false>(X, q, m, m_sel, l_slot, acc, a.scale_log2, slot_id, kBlock,
+                                         sub);
         else
-          attend_block_rs<D, GC, true>(X, q, m, m_sel, l_slot, acc, slot_id, valid, sub);
+          attend_block_rs<T, D, GC, true>(X, q, m, m_sel, l_slot, acc, a.scale_log2, slot_id, valid,
+                                        sub);
       } else {
         if (valid >= kBlock)
           attend_block<T, D, GC, false>(X, q, m, l, acc, a.scale_log2, slot_id, kBlock);

@@ -1160,8 +1160,11 @@ static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const int wg = 4;  // waves per workgroup
   hipLaunchKernelGGL((decode_split_kernel<T, D, GC>), dim3((a.num_splits + wg - 1) / wg),
                      dim3(wg * kWave), 0, stream, a);
-  hipLaunchKernelGGL((decode_combine_kernel<T, D, GC>), dim3(a.B * a.h_kv * a.n_chunks),
-                     dim3(kCombineWaves * kWave), 0, stream, a);
+  // With one range the single wave walks every segment whole and stores (or
+  // zero-fills) every output itself: no segment is cut, so no second pass.
+  if (a.num_splits > 1)
+    hipLaunchKernelGGL((decode_combine_kernel<T, D, GC>), dim3(a.B * a.h_kv * a.n_chunks),
+                       dim3(kCombineWaves * kWave), 0, stream, a);
   return hipGetLastError();
 }
 

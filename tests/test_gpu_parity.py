@@ -114,11 +114,13 @@ def test_decode_zero_length_and_single_token():
     kc = res.k_cache.to(DEV)
     vc = res.v_cache.to(DEV)
     lens0 = torch.tensor([0, 40, 0], dtype=torch.int32)
-    out = ops.paged_decode_attention(w.dec_q.to(DEV), kc, vc, w.dec_block_tables.to(DEV),
-                                     lens0.to(DEV), 40, scale=w.scale).cpu()
-    assert torch.count_nonzero(out[0]) == 0 and torch.count_nonzero(out[2]) == 0
     ref = O.decode(pins.np64(w.dec_q), kc_ref, vc_ref, w.dec_block_tables.numpy(), lens0.numpy(), w.scale)
-    assert max_err(out, ref) <= TOL[w.dtype]
+    # with one range no second pass runs: the first pass zero-fills and stores
+    for splits in (0, 1):
+        out = ops.paged_decode_attention(w.dec_q.to(DEV), kc, vc, w.dec_block_tables.to(DEV),
+                                         lens0.to(DEV), 40, scale=w.scale, num_splits=splits).cpu()
+        assert torch.count_nonzero(out[0]) == 0 and torch.count_nonzero(out[2]) == 0
+        assert max_err(out, ref) <= TOL[w.dtype]
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 17, 64, 500, 2048, 5000])

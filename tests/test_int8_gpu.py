@@ -151,9 +151,11 @@ def test_decode_int8_zero_length_and_split_agreement():
     got, ref = _append(w, pools)
     dev = [t.to(DEV) for t in got]
     lens0 = torch.tensor([0, 40, 0, 2000], dtype=torch.int32)
-    out = _decode(w, dev, 0, lens0)
-    assert torch.count_nonzero(out[0]) == 0 and torch.count_nonzero(out[2]) == 0
-    assert max_err(out, _oracle_decode(w, ref, lens0)) <= TOL
+    # also with one range, where no second pass runs: the first pass zero-fills
+    for splits in (0, 1):
+        out = _decode(w, dev, splits, lens0)
+        assert torch.count_nonzero(out[0]) == 0 and torch.count_nonzero(out[2]) == 0
+        assert max_err(out, _oracle_decode(w, ref, lens0)) <= TOL
     a = _decode(w, dev, 1)
     for splits in (2, 7, 64, 0):
         assert max_err(_decode(w, dev, splits), a.double().numpy()) <= TOL
@@ -202,6 +204,54 @@ def test_decode_int8_offset_queries():
         err = max_err(out, _oracle_decode(w, ref))
         print(f"q = 50 + N(0,1), splits {splits}: max|err| {err:.3e}")
         assert err <= TOL, f"int8 decode max|err| {err} with offset queries"
+
+
+def _term_err(got: torch.Tensor, ref: np.ndarray, ref_abs: np.ndarray) -> float:
+    """Largest error over max(1, attention over |V|): each output is a weighted
+    sum whose terms can cancel, and rounding each weight to bf16 errs by up to
+    2^-9 of that term, so the error scales with the sum of the terms'
+    magnitudes, not with the (possibly cancelled) result."""
+    g = got.to(torch.float64).numpy()
+    assert not np.isnan(g).any(), "NaN in GPU output"
+    return float((np.abs(g - ref) / np.maximum(1.0, ref_abs)).max()) if g.size else 0.0
+
+
+@pytest.mark.parametrize("wide_k", [False, True])
+def test_int8_wide_scales(wide_k):
+    """V scales drawn log-uniformly over [1e-4, 10] (and K scales too with
+    wide_k), unused slots' scales NaN: decode and prefill over the cache.  The
+    outputs reach a few hundred, and with random-sign codes a sum of large
+    terms can cancel to near zero, so the bound is 2e-2 times max(1, the
+    oracle's attention over |V|): in decode and prefill alike each softmax
+    weight times its token's V scale is rounded to bf16 once, an error of at
+    most 2^-9 of its term."""
+    rng = np.random.default_rng(4200 + wide_k)
+    w = W.build("wide", rng, dtype="bf16", h_q=32, h_kv=8, d=128,
+                decode_lens=[1, 17, 300, 1000, 2500], prefill=[(700, 300), (90, 33)],
+                free_frac=0.2, poison=True)
+    pools = W.int8_pools(w, seed=15, poison=True)
+
+    def wide(t: torch.Tensor) -> torch.Tensor:
+        x = t.numpy().copy()
+        nan = np.isnan(x)
+        x = (10.0 ** rng.uniform(-4.0, 1.0, size=x.shape)).astype(np.float32)
+        x[nan] = np.nan
+        return torch.from_numpy(x)
+
+    pools.v_scales = wide(pools.v_scales)
+    if wide_k:
+        pools.k_scales = wide(pools.k_scales)
+    got, ref = _append(w, pools)
+    _check_append_exact(got, ref)
+    dev = [t.to(DEV) for t in got]
+    kq, vq, ks, vs = ref
+    ref_abs = (kq, np.abs(vq), ks, vs)
+    o_dec, a_dec = _oracle_decode(w, ref), _oracle_decode(w, ref_abs)
+    e_dec = max(_term_err(_decode(w, dev, splits), o_dec, a_dec) for splits in (0, 7))
+    e_pre = _term_err(_prefill(w, dev), _oracle_prefill(w, ref), _oracle_prefill(w, ref_abs))
+    print(f"wide scales (K too: {wide_k}): decode {e_dec:.3e}, prefill {e_pre:.3e} "
+          "(over attention of |V|)")
+    assert e_dec <= 2e-2 and e_pre <= 2e-2
 
 
 # ----------------------------------------------------------------------------- prefill

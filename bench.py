@@ -32,7 +32,9 @@ Printed as one JSON line:
              Llama-3-8B shape (32/8/128) and the Qwen2.5-0.5B shape (14/2/64),
              where the kernel is not launch-bound; TFLOP/s against 2.5 PFLOP/s
   verify_decode  the chunked-prefill call with 4 new tokens per sequence of the
-             decode batch (a speculative verify step), in KV GB/s
+             decode batch (a speculative verify step), in KV GB/s; median of 5
+             batches of back-to-back calls after 30 warm-up calls, like the
+             INT8 verify
   int8_decode  paged_decode_attention_int8 on the same decode step over an
              INT8 cache: bytes = sum_b L_b * 2 * h_kv * (d_h + 4) (codes and
              one float32 scale per token head row), time over back-to-back
@@ -268,6 +270,25 @@ def time_calls(fn, iters: int, warmup: int = 3) -> float:
     return a.elapsed_time(b) / iters
 
 
+def time_batches(fn, iters: int, warmup: int = 30, batches: int = 5):
+    """Duration of one call: after `warmup` calls (the first calls after set-up
+    run a few percent slower), `batches` batches of `iters` back-to-back calls
+    between two HIP events.  Returns (median ms, [per-batch ms])."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(batches):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(iters):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) / iters)
+    return statistics.median(per), per
+
+
 def time_prefill(r: Resident, iters: int = 50, warmup: int = 5):
     """Average duration of one prefill call over `iters` back-to-back calls (two
     HIP events on the launch stream), and the per-call event durations of
@@ -344,11 +365,12 @@ def time_int8_prefill(dev: str, w5: W.Workload, iters: int):
     call = ops.bind_prefill_int8(wv.pre_q.to(dev), wv.pre_cu_seqlens.to(dev), *p8,
                                  wv.pre_block_tables.to(dev), wv.pre_context_lens.to(dev),
                                  wv.pre_max_q_len, scale=wv.scale)
-    ms = time_calls(lambda i: call(), iters, warmup=5)
+    ms, per = time_batches(lambda i: call(), max(iters // 5, 10))
     b8 = kv_bytes_int8_prefill(wv)
     res["verify"] = {"workload": "the 4 newest tokens of each of the decode batch's 64 sequences "
                                  "over an INT8 cache (codes + scales)", "bytes": b8,
-                     "avg_us": round(ms * 1e3, 2), "GBps": round(b8 / (ms / 1e3) / 1e9, 1),
+                     "avg_us": round(ms * 1e3, 2), "batches_us": [round(x * 1e3, 2) for x in per],
+                     "GBps": round(b8 / (ms / 1e3) / 1e9, 1),
                      "frac": round(b8 / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
     del p8, call
     torch.cuda.empty_cache()
@@ -840,7 +862,7 @@ def main(argv=None):
                  h_kv=wk.h_kv, d=wk.d, decode_lens=[],
                  prefill=[(int(L), 4) for L in wk.dec_context_lens], free_frac=0.1)
     rv = Resident(wv, dev, copies=args.copies)
-    v_ms = time_calls(rv.prefill, args.steps, warmup=5)
+    v_ms, v_batches = time_batches(rv.prefill, max(args.steps // 5, 10))
     progress("int8 decode and verify legs")
     kvbv = int(wv.pre_context_lens.to(torch.int64).sum()) * 2 * wv.h_kv * wv.d * wv.elem_bytes
     del rv
@@ -947,6 +969,7 @@ def main(argv=None):
                         "sequences attend causally over their caches (chunked-prefill call)",
             "kv_bytes": kvbv,
             "avg_us": round(v_ms * 1e3, 2),
+            "batches_us": [round(x * 1e3, 2) for x in v_batches],
             "GBps": round(kvbv / (v_ms / 1e3) / 1e9, 1),
             "frac": round(kvbv / (v_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         },

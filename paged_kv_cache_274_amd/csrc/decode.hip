@@ -703,15 +703,16 @@ __device__ __forceinline__ ScanResult scan_blocks(const DecodeArgs& a, int b, in
 // are wave wa's last-segment slot and the first-segment slots of the non-empty
 // waves wa + 1 .. wb (all waves are non-empty when the line has at least as many
 // blocks as splits).  Run by one whole wave.  The pieces' (max, sum) and the
-// first eight pieces' accumulators are requested together, before any of them
-// is used, so a merge of up to eight pieces costs one memory round trip.
-template <typename T, int D, int GC>
+// first kBatch pieces' accumulators are requested together, before any of them
+// is used, so a merge of up to kBatch pieces costs one memory round trip
+// (kBatch = 32 for a long context cut over many waves; 8 otherwise, which
+// keeps the unrolled loads and sums short).
+template <typename T, int D, int GC, int kBatch>
 __device__ __forceinline__ void merge_segment_head(const DecodeArgs& a, const Line& line, int b,
                                                    int head0, int j, int wa, int wb, int lane) {
   const int np = wb - wa + 1;
   const bool all_live = line.total >= line.splits;
   constexpr int CPL = (D + kWave - 1) / kWave;  // channels per lane
-  constexpr int kBatch = 8;
   auto piece = [&](int k) -> const float* {
     return a.ws + ((size_t)((wa + k) * 2 + (k == 0 ? 1 : 0)) * GC + j) * (D + 2);
   };
@@ -1151,8 +1152,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const Line line{*a.line_total, a.num_splits};
   const int wa = wr.x;
   const int wb = wr.y;
-  for (int j = wave; j < nh; j += kCombineWaves)
-    merge_segment_head<T, D, GC>(a, line, b, head0, j, wa, wb, lane);
+  if (wb - wa < 8) {
+    for (int j = wave; j < nh; j += kCombineWaves)
+      merge_segment_head<T, D, GC, 8>(a, line, b, head0, j, wa, wb, lane);
+  } else {
+    for (int j = wave; j < nh; j += kCombineWaves)
+      merge_segment_head<T, D, GC, 32>(a, line, b, head0, j, wa, wb, lane);
+  }
 }
 
 template <typename T, int D, int GC>

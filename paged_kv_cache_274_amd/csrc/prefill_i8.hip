@@ -376,15 +376,20 @@ __global__ __launch_bounds__(256) void prefill_i8_few_rows_kernel(PrefillArgs a)
   float* const ksc = reinterpret_cast<float*>(cbf + kChunkBf);          // sanitised scales
   float* const vsc = ksc + kI8FewKeys;
 
-  // Copies chunk c (blocks 2c, 2c + 1): codes of K then V (rows = keys, D
-  // bytes each), then the blocks' K and V scales (16 each, lanes 0-3 / 4-7 of
-  // one copy per block: block b at floats 32 b .. 32 b + 31, K then V).
-  auto issue_chunk = [&](int c, int st) {
+  // Raw table entry of block b (0 or 1) of chunk c, a scalar load; clamped
+  // where it is used, so the load has an iteration to land.
+  auto entry = [&](int c, int b) {
+    return constant_view(trow)[min(2 * c + b, a.max_blocks_per_seq - 1)];
+  };
+  // Copies a chunk (blocks with table entries e0 and e1): codes of K then V
+  // (rows = keys, D bytes each), then the blocks' K and V scales (16 each,
+  // lanes 0-3 / 4-7 of one copy per block: block b at floats 32 b .. 32 b + 31,
+  // K then V).
+  auto issue_chunk = [&](int st, int e0, int e1) {
     unsigned char* dst = mine + st * kStage;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int bi = min(2 * c + b, a.max_blocks_per_seq - 1);
-      int blk = constant_view(trow)[bi];
+      int blk = b == 0 ? e0 : e1;
       blk = (blk >= 0 && blk < a.n_blocks) ? blk : 0;
       const size_t bh = (size_t)blk * a.h_kv + kvh;
 #pragma unroll
@@ -448,10 +453,18 @@ __global__ __launch_bounds__(256) void prefill_i8_few_rows_kernel(PrefillArgs a)
   const int tr_row = 4 * (grp >> 1) + ((lane & 15) >> 2);
   const int tr_ch = 16 * (grp & 1) + 4 * (lane & 3);
 
-  if (wave < n_chunks) issue_chunk(wave, 0);
+  if (wave < n_chunks) issue_chunk(0, entry(wave, 0), entry(wave, 1));
+  // Entries of the chunk after next are requested an iteration before their
+  // copies are issued.
+  int n0 = entry(wave + kPfWaves, 0);
+  int n1 = entry(wave + kPfWaves, 1);
   for (int c = wave, st = 0; c < n_chunks; c += kPfWaves, st ^= 1) {
     const bool more = c + kPfWaves < n_chunks;
-    if (more) issue_chunk(c + kPfWaves, st ^ 1);
+    if (more) {
+      issue_chunk(st ^ 1, n0, n1);
+      n0 = entry(c + 2 * kPfWaves, 0);
+      n1 = entry(c + 2 * kPfWaves, 1);
+    }
     if (more)
       wait_vm<kCopies>();
     else

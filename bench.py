@@ -10,13 +10,16 @@ shuffled); --config 4 selects the long-context batch (B=8, L=8192, 13 shared
 prefix blocks).  Inputs are seeded synthetic data already resident in HBM;
 three copies of the pool are rotated so that no step finds its KV data in the
 256 MB Infinity Cache or the L2s left by the step before.  K steps are timed
-with wall clock between two synchronisations.
+with wall clock between two synchronisations, after W untimed steps; the
+roofline leg runs before them, so the GPU is at its steady clocks.  Every
+other leg is timed after at least 50 ms of untimed calls of its own kind (the
+first milliseconds of load run at lower clocks).
 
 Printed as one JSON line:
   value      KV bytes attended per second (GB/s), whole step (append + decode)
   roofline   the decode call (its two kernels; HIP events on the launch stream
              around each of 5 batches of max(K, 20) back-to-back calls after
-             the timed steps and 50 warm-up calls, median batch; in_step_* from
+             at least 50 warm-up calls and 50 ms, median batch; in_step_* from
              events around each call of K more steps) against the 8 TB/s HBM
              peak; algorithmic bytes per
              call = sum_b L_b * 2 * h_kv * d_h * 2 B (the KV-cache footprint
@@ -177,6 +180,24 @@ class Resident:
         self._prefill_calls[i % len(self.pools)]()
 
 
+WARM_MS = 50.0
+
+
+def warm_up(fn, calls: int, min_ms: float = WARM_MS) -> None:
+    """Untimed calls: at least `calls`, and more until `min_ms` of wall time has
+    passed (synchronising every 16 calls so that the host does not run ahead).
+    The GPU reaches its steady clocks only after some milliseconds of load, so a
+    fixed call count leaves a 50 us call measured at lower clocks."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < calls or (time.perf_counter() - t0) * 1e3 < min_ms:
+        fn(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def time_steps(r: Resident, steps: int, warmup: int) -> float:
     """Wall time of `steps` whole steps (append + decode), nothing else queued."""
     for i in range(warmup):
@@ -210,11 +231,9 @@ def time_step_parts(r: Resident, steps: int):
 def time_decode_calls(r: Resident, iters: int, warmup: int = 50, batches: int = 5):
     """Duration of one decode call: two HIP events on the launch stream around
     each of `batches` batches of `iters` back-to-back calls (no per-call event
-    overhead), after `warmup` calls (the first few dozen calls after the
-    pools are set up run about 5% slower).  Returns (median, [per-batch ms])."""
-    for i in range(warmup):
-        r.decode(i)
-    torch.cuda.synchronize()
+    overhead), after at least `warmup` calls and WARM_MS of untimed calls (the
+    first milliseconds run at lower clocks).  Returns (median, [per-batch ms])."""
+    warm_up(r.decode, warmup)
     per = []
     for _ in range(batches):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -257,10 +276,11 @@ def progress(what: str) -> None:
 
 
 def time_calls(fn, iters: int, warmup: int = 3) -> float:
-    """Average ms of one call over `iters` back-to-back calls (two HIP events)."""
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
+    """Average ms of one call over `iters` back-to-back calls (two HIP events),
+    after at least `warmup` calls and WARM_MS of untimed calls (none if
+    `warmup` is 0: the caller has warmed up)."""
+    if warmup > 0:
+        warm_up(fn, warmup)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(iters):
@@ -271,12 +291,11 @@ def time_calls(fn, iters: int, warmup: int = 3) -> float:
 
 
 def time_batches(fn, iters: int, warmup: int = 30, batches: int = 5):
-    """Duration of one call: after `warmup` calls (the first calls after set-up
-    run a few percent slower), `batches` batches of `iters` back-to-back calls
-    between two HIP events.  Returns (median ms, [per-batch ms])."""
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
+    """Duration of one call: after at least `warmup` calls and WARM_MS of
+    untimed calls (the first milliseconds run at lower clocks), `batches`
+    batches of `iters` back-to-back calls between two HIP events.  Returns
+    (median ms, [per-batch ms])."""
+    warm_up(fn, warmup)
     per = []
     for _ in range(batches):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -290,19 +309,12 @@ def time_batches(fn, iters: int, warmup: int = 30, batches: int = 5):
 
 
 def time_prefill(r: Resident, iters: int = 50, warmup: int = 5):
-    """Average duration of one prefill call over `iters` back-to-back calls (two
-    HIP events on the launch stream), and the per-call event durations of
-    single calls, which add the event overhead to a kernel of a few us."""
-    for i in range(warmup):
-        r.prefill(i)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(iters):
-        r.prefill(i)
-    b.record()
-    torch.cuda.synchronize()
-    back_to_back_ms = a.elapsed_time(b) / iters
+    """Duration of one prefill call: the median of 5 batches of `iters`
+    back-to-back calls (two HIP events on the launch stream each) after at
+    least `warmup` calls and WARM_MS of untimed calls, and the per-call event
+    durations of single calls, which add the event overhead to a kernel of a
+    few us.  Returns (median ms, [per-call ms], [per-batch ms])."""
+    back_to_back_ms, batches = time_batches(r.prefill, iters, warmup)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(iters)]
     for i in range(iters):
@@ -310,21 +322,21 @@ def time_prefill(r: Resident, iters: int = 50, warmup: int = 5):
         r.prefill(i)
         ev[i][1].record()
     torch.cuda.synchronize()
-    return back_to_back_ms, [a.elapsed_time(b) for a, b in ev]
+    return back_to_back_ms, [a.elapsed_time(b) for a, b in ev], batches
 
 
 def time_long_prefill(dev: str, iters: int = 5, warmup: int = 30, batches: int = 5):
     """prefill_long: 4 x 4096-token causal prefills at each shape of
-    LONG_PREFILL; after `warmup` calls (the first calls run 10-20% slower),
-    `batches` batches of `iters` back-to-back calls between two HIP events;
-    the median batch, with every batch listed."""
+    LONG_PREFILL; after at least `warmup` calls and WARM_MS of untimed calls
+    (the first calls run 10-20% slower), `batches` batches of `iters`
+    back-to-back calls between two HIP events; the median batch, with every
+    batch listed."""
     res = {}
     for (h_q, h_kv, d), name in LONG_PREFILL.items():
         w = W.long_prefill(h_q, h_kv, d)
         r = Resident(w, dev)
         r.append(0)
-        for i in range(warmup):
-            r.prefill(i)
+        warm_up(r.prefill, warmup)
         per = [time_calls(r.prefill, iters, warmup=0) for _ in range(batches)]
         ms = statistics.median(per)
         fl = prefill_flops(w)
@@ -678,6 +690,9 @@ def summarize_mfma(csv_path, steps, what="prefill"):
     return "\n".join(text) + "\n"
 
 
+N_STATS_CALLS = 200  # decode calls of the stats summary (all after the warm-up)
+
+
 def summarize_stats(stats_csv, bench_json, extra):
     with open(bench_json) as f:
         line = json.loads([s for s in f.read().splitlines() if s.startswith("{")][-1])
@@ -695,10 +710,13 @@ def summarize_stats(stats_csv, bench_json, extra):
     call_ns = sum(float(r["AverageNs"]) for r in split + comb)
     trace = os.path.join(os.path.dirname(stats_csv),
                          os.path.basename(stats_csv).replace("kernel_stats", "kernel_trace"))
+    n_warm = None
     if os.path.exists(trace):
         # the long-context leg runs the same kernels later in the run: the
-        # timed batch's calls are those dispatched before the first INT8 decode
-        # (the bench runs its legs in a fixed order)
+        # decode batch's calls are those dispatched before the first INT8
+        # decode (the bench runs its legs in a fixed order); the last
+        # N_STATS_CALLS of them come after the untimed warm-up (roofline
+        # batches, timed steps and step parts)
         with open(trace) as f:
             ds = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
         first_i8 = next((i for i, r in enumerate(ds) if "decode_" in r["Kernel_Name"] and
@@ -708,7 +726,8 @@ def summarize_stats(stats_csv, bench_json, extra):
         sp = [dur(r) for r in early if "decode_split_kernel" in r["Kernel_Name"]]
         cb = [dur(r) for r in early if "decode_combine_kernel" in r["Kernel_Name"]]
         if sp and cb:
-            call_ns = statistics.mean(sp) + statistics.mean(cb)
+            n_warm = max(0, min(len(sp), len(cb)) - N_STATS_CALLS)
+            call_ns = statistics.mean(sp[n_warm:]) + statistics.mean(cb[n_warm:])
     i8 = [r for r in rows if "decode_" in r["Name"] and f"i8_t, {d_h}," in r["Name"]]
     i8_ns = sum(float(r["AverageNs"]) for r in i8)
     text = [
@@ -741,7 +760,9 @@ def summarize_stats(stats_csv, bench_json, extra):
             text.append(f"#   {len(v):4d} {statistics.median(v):10.2f} {min(v):10.2f}  "
                         f"{legs.get(n, f'{n} pairs')}")
     text += [
-        f"# decode call of the timed batch = split pass + combine pass averages over its dispatches: {call_ns / 1e3:.2f} us (rocprofv3 kernel trace);",
+        f"# decode call of the decode batch = split pass + combine pass averages over its last "
+        f"{N_STATS_CALLS} dispatches each (after {n_warm} warm-up calls): {call_ns / 1e3:.2f} us "
+        "(rocprofv3 kernel trace);",
         f"# HIP events in the same run: {line['roofline']['avg_us']} us per call over back-to-back "
         f"calls, {line['roofline']['in_step_avg_us']} us around single calls inside the steps",
         f"# INT8-cache decode call (split + combine averages over all its calls, warm-up included): {i8_ns / 1e3:.2f} us;"
@@ -834,11 +855,13 @@ def main(argv=None):
 
     wk = W.config(args.config)
     rk = Resident(wk, dev, copies=args.copies)
+    # The roofline leg runs first: its untimed warm-up also brings the GPU to
+    # its steady clocks before the W warm-up and K timed steps of the headline.
+    dec_med_ms, dec_batches_ms = time_decode_calls(rk, max(args.steps, 20))
     wall = time_steps(rk, args.steps, args.warmup)
     progress("timed decode steps")
     kvb = kv_bytes(wk)
     value = kvb * args.steps / wall / 1e9
-    dec_med_ms, dec_batches_ms = time_decode_calls(rk, max(args.steps, 20))
     dec_avg_s = dec_med_ms / 1e3
     app_ms, dec_ms = time_step_parts(rk, args.steps)
     progress("decode roofline leg")
@@ -882,7 +905,7 @@ def main(argv=None):
     w5 = W.config(5)
     r5 = Resident(w5, dev)
     r5.append(0)
-    pf_b2b_ms, pf_ms = time_prefill(r5)
+    pf_b2b_ms, pf_ms, pf_batches = time_prefill(r5)
     int8_prefill = time_int8_prefill(dev, w5, args.steps)
 
     # the whole mixed continuous-batch step of the same workload: append of all
@@ -1005,6 +1028,7 @@ def main(argv=None):
                         "d_h=64, causal, bf16",
             "flops": prefill_flops(w5),
             "avg_us": round(pf_avg_s * 1e6, 2),
+            "batches_us": [round(x * 1e3, 2) for x in pf_batches],
             "single_call_event_median_us": round(pct(pf_ms, 50) * 1e3, 2),
             "tflops": round(pf_tflops, 3),
             "peak_tflops": BF16_MFMA_PEAK_TFLOPS,

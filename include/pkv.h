@@ -70,7 +70,9 @@ typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_INT8 = 2 } pkv_dtype;
 typedef enum {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad device value (PKV_DEBUG) */
-  PKV_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (d_h, dtype) */
+  PKV_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (d_h, dtype), or beyond the
+                              size limits: block tables wider than 2^27 - 1 blocks (2^31
+                              tokens), decode lines of more than 2^40 block reads */
   PKV_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
   PKV_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
   PKV_ERR_NO_BLOCKS = 5    /* block manager: not enough free blocks; nothing changed */
@@ -127,9 +129,11 @@ int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
  *                  matter.  The caller owns it and must not use it
  *                  concurrently with the call.
  * The blocks of all (sequence, KV head) pairs, laid end to end, are cut into
- * one equal range per wavefront the device holds at once; results do not
- * depend on the cut beyond fp32 rounding.  B == 0 enqueues nothing.  Requires
- * h_q % h_kv == 0, d_h in {64, 128}.
+ * one range per wavefront the device holds at once (ranges of wavefronts on
+ * even XCDs 11/10 the size of those on odd XCDs, which run slower); results
+ * do not depend on the cut beyond fp32 rounding.  B == 0 enqueues nothing.
+ * Requires h_q % h_kv == 0, d_h in {64, 128}; returns PKV_ERR_UNSUPPORTED
+ * when B * h_kv * ceil(max_context_len / 16) exceeds 2^40 block reads.
  */
 int paged_decode_attention(void* out, const void* q,
                            const void* k_cache, const void* v_cache,
@@ -148,7 +152,8 @@ size_t pkv_decode_workspace_bytes(int B, int h_q, int d_h, int max_context_len);
  * paged_decode_attention_split - paged_decode_attention with the number of
  * ranges set by the caller (for tuning and for tests of the merge):
  *   num_splits : 0 picks the split automatically (as paged_decode_attention);
- *                  otherwise 1 .. 65536 equal ranges.
+ *                  otherwise 1 .. 65536 ranges, weighted as in
+ *                  paged_decode_attention (one range: the whole line).
  *   workspace : at least pkv_decode_workspace_bytes_split(B, h_q, h_kv, d_h,
  *                  max_context_len, dtype, num_splits) bytes.
  */

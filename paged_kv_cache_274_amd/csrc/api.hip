@@ -12,6 +12,9 @@
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Widest block-table row: its token capacity (16 per block) stays an int, as
+// the kernels clamp context lengths to it in 32-bit arithmetic.
+constexpr int kMaxTableWidth = 0x7fffffff / 16;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -45,7 +48,7 @@ int debug_check_tables(const int32_t* tables, const int32_t* lens, int n_seqs, i
   if (!copy_to_host(t, tables, (size_t)n_seqs * max_blocks, stream)) return PKV_ERR_HIP;
   for (int s = 0; s < n_seqs; ++s) {
     if (l[s] < 0 || l[s] > max_len) return PKV_ERR_INVALID_ARG;
-    for (int j = 0; j < (l[s] + 15) / 16; ++j) {
+    for (int64_t j = 0; j < ((int64_t)l[s] + 15) / 16; ++j) {
       const int32_t e = t[(size_t)s * max_blocks + j];
       if (e < 0 || e >= n_blocks) return PKV_ERR_INVALID_ARG;
     }
@@ -314,12 +317,14 @@ static int decode_call(void* out, const void* q, const void* k_cache, const void
       max_blocks_per_seq <= 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * 16 ||
       !isfinite(scale))
     return PKV_ERR_INVALID_ARG;
-  if (d_h != 64 && d_h != 128) return PKV_ERR_UNSUPPORTED;
+  if ((d_h != 64 && d_h != 128) || max_blocks_per_seq > kMaxTableWidth) return PKV_ERR_UNSUPPORTED;
   if (B == 0) return PKV_OK;
   const bool i8 = kv == pkv::KvType::kI8;
   const bool bf16 = chunks_as_bf16(kv);
   const pkv::HeadChunks hc = pkv::head_chunks(h_q / h_kv, d_h, bf16, B, h_kv, max_context_len);
-  if ((int64_t)B * h_kv * hc.n_chunks > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)B * h_kv * hc.n_chunks > 0x7fffffff ||
+      pkv::decode_line_upper(B, h_q, h_kv, d_h, bf16, max_context_len) > pkv::kMaxLineBlocks)
+    return PKV_ERR_UNSUPPORTED;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens ||
       (i8 && (!k_scale || !v_scale)))
     return PKV_ERR_INVALID_ARG;
@@ -440,7 +445,7 @@ int paged_prefill_attention(void* out, const void* q, const int32_t* cu_seqlens_
   if (S < 0 || T_q < 0 || max_q_len < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0 ||
       n_blocks <= 0 || max_blocks_per_seq <= 0 || !isfinite(scale))
     return PKV_ERR_INVALID_ARG;
-  if (d_h != 64 && d_h != 128) return PKV_ERR_UNSUPPORTED;
+  if ((d_h != 64 && d_h != 128) || max_blocks_per_seq > kMaxTableWidth) return PKV_ERR_UNSUPPORTED;
   if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
   if (S == 0 || T_q == 0 || max_q_len == 0) return PKV_OK;
   if (S > 65535 || h_kv > 65535) return PKV_ERR_UNSUPPORTED;
@@ -494,7 +499,7 @@ int paged_prefill_attention_int8(void* out, const void* q, const int32_t* cu_seq
   if (S < 0 || T_q < 0 || max_q_len < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0 ||
       n_blocks <= 0 || max_blocks_per_seq <= 0 || !isfinite(scale))
     return PKV_ERR_INVALID_ARG;
-  if (d_h != 64 && d_h != 128) return PKV_ERR_UNSUPPORTED;
+  if ((d_h != 64 && d_h != 128) || max_blocks_per_seq > kMaxTableWidth) return PKV_ERR_UNSUPPORTED;
   if (S == 0 || T_q == 0 || max_q_len == 0) return PKV_OK;
   if (S > 65535 || h_kv > 65535) return PKV_ERR_UNSUPPORTED;
   if (!out || !q || !cu_seqlens_q || !k_cache || !v_cache || !k_scale || !v_scale ||

@@ -36,7 +36,7 @@ constexpr int kSmallLineBlocksPerWave = 16;
 inline HeadChunks head_chunks(int g, int d_h, bool bf16, int B, int h_kv, int max_context_len) {
   const int cap = max_chunk(d_h, bf16);
   if (g > 4 && cap > 4) {
-    const int64_t line4 = (int64_t)B * h_kv * ((g + 3) / 4) * ((max_context_len + 15) / 16);
+    const int64_t line4 = (int64_t)B * h_kv * ((g + 3) / 4) * (((int64_t)max_context_len + 15) / 16);
     if (line4 <= (int64_t)kSmallLineWaves * kSmallLineBlocksPerWave) return chunks_of(g, 4);
   }
   return chunks_of(g, cap);
@@ -48,13 +48,16 @@ inline int64_t decode_line_upper(int B, int h_q, int h_kv, int d_h, bool bf16,
                                  int max_context_len) {
   return (int64_t)B * h_kv *
          head_chunks(h_q / h_kv, d_h, bf16, B, h_kv, max_context_len).n_chunks *
-         ((max_context_len + 15) / 16);
+         (((int64_t)max_context_len + 15) / 16);
 }
 
 // Upper bound of the automatic split count (resident wavefronts of a full MI355X
 // at two waves per SIMD is 2048; the bound leaves room for higher occupancy).
 constexpr int kMaxAutoSplits = 4096;
 constexpr int kMaxSplits = 1 << 16;
+// Longest line the decode cuts: positions times the cut's cumulative weights
+// (at most kMaxSplits * 11) stay within int64.
+constexpr int64_t kMaxLineBlocks = (int64_t)1 << 40;
 
 // Splits the workspace must hold: the explicit count, or the automatic bound.
 inline int64_t decode_split_bound(int B, int h_q, int h_kv, int d_h, bool bf16,
@@ -91,7 +94,7 @@ inline size_t decode_workspace_bytes(int B, int h_q, int h_kv, int d_h, bool bf1
 inline size_t decode_workspace_bound(int B, int h_q, int d_h, int max_context_len) {
   if (B <= 0) return 0;
   const int64_t segs = (int64_t)B * h_q;
-  int64_t splits = segs * ((max_context_len + 15) / 16);
+  int64_t splits = segs * (((int64_t)max_context_len + 15) / 16);
   splits = splits < 1 ? 1 : (splits > kMaxAutoSplits ? kMaxAutoSplits : splits);
   const int gc = h_q < 8 ? h_q : 8;
   return (size_t)splits * 2 * gc * (size_t)(d_h + 2) * sizeof(float) +

@@ -96,6 +96,14 @@ def test_decode_validation():
     assert _decode(ws_bytes=exact - 1) == 3
     assert _decode(ws=MISALIGNED) == 3
     assert _decode(B=0, out=None, q=None) == 0
+    # a line of more than 2^40 block reads (B * h_kv * ceil(max_context_len / 16))
+    # is refused before any pointer is looked at
+    assert _decode(B=1 << 16, h_q=8, h_kv=8, maxc=((1 << 27) - 1) * 16, mb=(1 << 27) - 1,
+                   out=None, q=None) == 2
+    assert _decode(B=1 << 16, h_q=8, h_kv=8, maxc=1 << 30, mb=1 << 26, out=None, q=None) == 2
+    assert _decode(B=1 << 10, h_q=8, h_kv=8, maxc=1 << 30, mb=1 << 26, out=None) == 1
+    # block-table rows whose token capacity would not fit an int
+    assert _decode(mb=1 << 27, out=None) == 2
 
 
 def test_decode_split_validation():
@@ -168,6 +176,7 @@ def test_prefill_validation():
     assert _prefill(q=MISALIGNED) == 1
     assert _prefill(S=0, out=None) == 0
     assert _prefill(T_q=0, out=None) == 0
+    assert _prefill(mb=1 << 27, out=None) == 2   # row capacity past an int
 
 
 @pytest.mark.parametrize("B,h_q,h_kv,d,maxc", [(64, 32, 8, 128, 4096), (8, 32, 8, 128, 8192),
@@ -256,6 +265,7 @@ def test_prefill_int8_validation():
     assert _prefill8(scale=float("inf")) == 1
     assert _prefill8(S=0, out=None) == 0
     assert _prefill8(T_q=0, out=None) == 0
+    assert _prefill8(mb=1 << 27, out=None) == 2
 
 
 def _ptrs(*vals):

@@ -242,6 +242,20 @@ int paged_decode_attention_int8(void* out, const void* q,
                                 int num_splits, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/* Inspection of the decode's cut (host-only, no HIP call; the kernels use the
+ * same code).  The blocks of all (sequence, KV head, head chunk) segments,
+ * laid end to end, form a line of `total` blocks, cut into `splits` ranges;
+ * wave w of the decode grid streams positions
+ * [pkv_decode_line_start(total, splits, w), ...start(total, splits, w + 1)).
+ * Waves 4k .. 4k + 3 run on XCD k mod 8, and a wave of an even XCD takes 11
+ * blocks for every 10 of a wave of an odd XCD (odd XCDs stream slower).
+ *   pkv_decode_line_start : 0 <= w <= splits; returns -1 on invalid arguments
+ *                           (total in 0 .. 2^40, splits in 1 .. 65536).
+ *   pkv_decode_line_wave_of : the wave whose range holds position p,
+ *                           0 <= p < total; -1 on invalid arguments. */
+int64_t pkv_decode_line_start(int64_t total, int splits, int w);
+int pkv_decode_line_wave_of(int64_t total, int splits, int64_t p);
+
 /* Number of splits a decode call uses for these arguments; -1 on invalid
  * arguments.  With num_splits == 0 it queries the current device's occupancy
  * for the decode kernel (2048 wavefronts are assumed when no device can be

@@ -7,6 +7,7 @@
 #include <vector>
 
 #include "launch.h"
+#include "line.h"
 #include "pkv.h"
 
 namespace {
@@ -247,6 +248,20 @@ static int auto_splits(int B, int h_q, int h_kv, int d_h, int max_context_len, p
   if (waves <= 0) waves = 2048;
   const int64_t bound = pkv::decode_split_bound(B, h_q, h_kv, d_h, bf16, max_context_len, 0);
   return (int)(waves < bound ? waves : bound);
+}
+
+int64_t pkv_decode_line_start(int64_t total, int splits, int w) {
+  if (total < 0 || total > pkv::kMaxLineBlocks || splits < 1 || splits > pkv::kMaxSplits ||
+      w < 0 || w > splits)
+    return -1;
+  return pkv::Line{total, splits}.start(w);
+}
+
+int pkv_decode_line_wave_of(int64_t total, int splits, int64_t p) {
+  if (total < 1 || total > pkv::kMaxLineBlocks || splits < 1 || splits > pkv::kMaxSplits ||
+      p < 0 || p >= total)
+    return -1;
+  return pkv::Line{total, splits}.wave_of(p);
 }
 
 int pkv_decode_num_splits(int B, int h_q, int h_kv, int d_h, int max_context_len, int dtype,

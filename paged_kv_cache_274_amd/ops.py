@@ -30,7 +30,8 @@ EXPORTED = ("kv_append", "paged_decode_attention", "paged_prefill_attention",
             "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_sequence", "pkv_bm_append",
             "pkv_bm_fork", "pkv_bm_free", "pkv_bm_swap_out", "pkv_bm_swap_in",
             "pkv_bm_block_table", "pkv_bm_get_stats", "pkv_kv_cache_bytes",
-            "pkv_bm_append_batch", "pkv_bm_block_tables")
+            "pkv_bm_append_batch", "pkv_bm_block_tables",
+            "pkv_decode_line_start", "pkv_decode_line_wave_of")
 PKV_ERR_NO_BLOCKS = 5
 
 _lib = None
@@ -71,6 +72,10 @@ def lib() -> ctypes.CDLL:
     L.kv_append.restype = i32
     L.pkv_decode_num_splits.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.pkv_decode_num_splits.restype = i32
+    L.pkv_decode_line_start.argtypes = [ctypes.c_int64, i32, i32]
+    L.pkv_decode_line_start.restype = ctypes.c_int64
+    L.pkv_decode_line_wave_of.argtypes = [ctypes.c_int64, i32, ctypes.c_int64]
+    L.pkv_decode_line_wave_of.restype = i32
     L.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.pkv_decode_workspace_bytes.restype = ctypes.c_size_t
     L.pkv_decode_workspace_bytes_split.argtypes = [i32, i32, i32, i32, i32, i32, i32]
@@ -199,6 +204,16 @@ def decode_num_splits(B: int, h_q: int, h_kv: int, d_h: int, max_context_len: in
     """dtype: the pool's (torch.int8 for the INT8 cache)."""
     return int(lib().pkv_decode_num_splits(B, h_q, h_kv, d_h, max_context_len, _WS_DTYPE[dtype],
                                            num_splits))
+
+
+def decode_line_start(total: int, splits: int, w: int) -> int:
+    """First line position of decode wave w (pkv_decode_line_start); -1 if invalid."""
+    return int(lib().pkv_decode_line_start(total, splits, w))
+
+
+def decode_line_wave_of(total: int, splits: int, p: int) -> int:
+    """The decode wave whose range holds line position p; -1 if invalid."""
+    return int(lib().pkv_decode_line_wave_of(total, splits, p))
 
 
 def decode_workspace_bytes(B: int, h_q: int, h_kv: int, d_h: int, max_context_len: int,

@@ -1,0 +1,65 @@
+"""The decode's cut of its work line (host logic, no GPU): the blocks of all
+(sequence, KV head, head chunk) segments laid end to end are split into one
+range per wave, waves of even XCDs taking 11 blocks for every 10 of a wave of
+an odd XCD.  The kernels run the same code; these tests pin its invariants
+through the library's inspection calls: the ranges tile the line in order,
+the inverse finds the range holding each position, sizes follow the weights
+to within rounding, every range is non-empty from three blocks per wave, and
+invalid arguments are refused."""
+import pytest
+
+from paged_kv_cache_274_amd import ops
+
+start = ops.decode_line_start
+wave_of = ops.decode_line_wave_of
+
+
+def _cut(total, splits):
+    return [start(total, splits, w) for w in range(splits + 1)]
+
+
+@pytest.mark.parametrize("splits", list(range(1, 20)) + [31, 64, 100])
+def test_ranges_tile_the_line_and_invert(splits):
+    for total in list(range(0, 60)) + [61, 250, 999]:
+        cut = _cut(total, splits)
+        assert cut[0] == 0 and cut[-1] == total
+        assert all(a <= b for a, b in zip(cut, cut[1:]))
+        if total >= 3 * splits:
+            assert all(a < b for a, b in zip(cut, cut[1:])), (total, splits)
+        for p in range(total):
+            w = wave_of(total, splits, p)
+            assert 0 <= w < splits and cut[w] <= p < cut[w + 1], (total, splits, p, w)
+
+
+@pytest.mark.parametrize("total,splits", [(77500, 2048), (32768, 2048), (1 << 30, 4096),
+                                          (155000, 2047), ((1 << 40) - 1, 65536)])
+def test_large_lines(total, splits):
+    cut = _cut(total, splits)
+    assert cut[0] == 0 and cut[-1] == total
+    sizes = [b - a for a, b in zip(cut, cut[1:])]
+    assert min(sizes) > 0
+    # waves 4k .. 4k + 3 run on XCD k mod 8: even XCDs take 11/10 of an odd XCD's share
+    even = [s for w, s in enumerate(sizes) if (w >> 2) % 2 == 0]
+    odd = [s for w, s in enumerate(sizes) if (w >> 2) % 2 == 1]
+    ratio = (sum(even) / len(even)) / (sum(odd) / len(odd))
+    assert abs(ratio - 1.1) < 1.1 / min(sizes) + 1e-9, ratio
+    for p in [0, 1, total // 3, total // 2, total - 2, total - 1] + [cut[w] for w in (1, 7, 8, splits - 1)]:
+        w = wave_of(total, splits, p)
+        assert cut[w] <= p < cut[w + 1]
+
+
+def test_one_split_is_the_whole_line():
+    assert _cut(12345, 1) == [0, 12345]
+    assert wave_of(12345, 1, 12344) == 0
+
+
+def test_invalid_arguments():
+    assert start(-1, 4, 0) == -1
+    assert start(10, 0, 0) == -1
+    assert start(10, 4, 5) == -1
+    assert start(10, 4, -1) == -1
+    assert start((1 << 40) + 1, 4, 1) == -1
+    assert start(10, (1 << 16) + 1, 1) == -1
+    assert wave_of(10, 4, 10) == -1
+    assert wave_of(10, 4, -1) == -1
+    assert wave_of(0, 4, 0) == -1

@@ -13,10 +13,11 @@
 //  * A segment is (sequence b, KV head, chunk of <= 8 query heads of its GQA
 //    group); it owns the ceil(L_b / 16) blocks of that KV head.  All segments'
 //    blocks are laid end to end (sequence-major) and the line is cut into
-//    num_splits equal contiguous ranges, one per wavefront.  With num_splits =
-//    the number of wavefronts the chip holds at once, every wave starts at once,
-//    does the same number of blocks whatever the length mix, and finishes at
-//    once; there is no per-partition prologue or tail.
+//    num_splits contiguous ranges, one per wavefront, sized by the speed of
+//    the XCD the wavefront runs on (line.h).  With num_splits = the number of
+//    wavefronts the chip holds at once, every wave starts at once, does its
+//    share of blocks whatever the length mix, and finishes with the others;
+//    there is no per-partition prologue or tail.
 //  * A wave walks its range block by block, crossing segment boundaries.  Each
 //    K/V block of a KV head is read once for all query heads of the chunk.
 //    A segment finished inside one wave is normalised and stored directly; a

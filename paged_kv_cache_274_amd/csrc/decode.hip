@@ -1062,11 +1062,16 @@ struct RangeStream {
   }
 };
 
+constexpr int kSplitWaves = 4;  // waves per workgroup of the split kernel
+
 template <typename T, int D, int GC>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kSplitWaves * kWave) void decode_split_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int W = blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  if (W >= a.num_splits) return;
+  // The wave index and the grid size come from compile-time and argument
+  // values, not from the dispatch's hidden arguments, so the kernel starts
+  // with a single round of scalar argument loads.
+  const int W = blockIdx.x * kSplitWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const bool in_grid = W < a.num_splits;  // the last workgroup may hold spare waves
   const int HC = a.h_kv * a.n_chunks;
   // Two workgroups share each CU, and the one dispatched second is younger on
   // every SIMD it shares; issue arbitration favours the older wave, so the
@@ -1075,10 +1080,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // the first three quarters of its range (measured on the Llama-3-8B-shaped
   // batch: 111.4 -> 109.2 us per call; priority over the whole range, or up
   // to half of it, gained less).
-  if (blockIdx.x >= gridDim.x / 2) __builtin_amdgcn_s_setprio(2);
+  if ((int)blockIdx.x >= (a.num_splits + kSplitWaves - 1) / kSplitWaves / 2)
+    __builtin_amdgcn_s_setprio(2);
 
   // Sequences of length 0 get an all-zero output (sequence b by wave b mod splits).
-  for (int b0 = W; b0 < a.B; b0 += a.num_splits) {
+  for (int b0 = W; in_grid && b0 < a.B; b0 += a.num_splits) {
     if (seq_len(a, b0) != 0) continue;
     OutOf<T>* out = reinterpret_cast<OutOf<T>*>(a.out) + (size_t)b0 * a.h_q * D;
     for (int i = lane; i < a.h_q * D; i += kWave) store_elem<OutOf<T>>(out, i, 0.f);
@@ -1087,7 +1093,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const ScanResult all = scan_blocks(a, -1, lane);
   const Line line{all.total * HC, a.num_splits};
   if (W == 0 && lane == 0) *a.line_total = line.total;  // for the second pass
-  if (line.total == 0) return;
+  if (line.total == 0 || !in_grid) return;
   const int64_t s = line.start(W);
   const int64_t e = line.start(W + 1);
   if (s >= e) return;
@@ -1159,9 +1165,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 
 template <typename T, int D, int GC>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  const int wg = 4;  // waves per workgroup
-  hipLaunchKernelGGL((decode_split_kernel<T, D, GC>), dim3((a.num_splits + wg - 1) / wg),
-                     dim3(wg * kWave), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, GC>),
+                     dim3((a.num_splits + kSplitWaves - 1) / kSplitWaves),
+                     dim3(kSplitWaves * kWave), 0, stream, a);
   // With one range the single wave walks every segment whole and stores (or
   // zero-fills) every output itself: no segment is cut, so no second pass.
   if (a.num_splits > 1)
@@ -1177,11 +1183,12 @@ static int occupancy_waves_t() {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(decode_split_kernel<T, D, GC>), 256, 0) !=
+            &per_cu, reinterpret_cast<const void*>(decode_split_kernel<T, D, GC>),
+            kSplitWaves * kWave, 0) !=
             hipSuccess ||
         cus <= 0 || per_cu <= 0)
       return 0;
-    return cus * per_cu * 4;
+    return cus * per_cu * kSplitWaves;
   }();
   return waves;
 }

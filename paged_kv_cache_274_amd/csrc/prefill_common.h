@@ -18,6 +18,7 @@ constexpr float kPfSlack = 8.0f;  // log2 units
 
 #define PKV_LDS __attribute__((address_space(3)))
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct PfTile {

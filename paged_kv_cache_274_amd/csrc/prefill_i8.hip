@@ -314,16 +314,24 @@ __global__ __launch_bounds__(256) void prefill_i8_kernel(PrefillArgs a) {
 // Few query rows per (sequence, KV head) (at most 32: multi-token decode), as
 // prefill_few_rows_kernel in prefill.hip: the 4 waves split the key walk into
 // 32-key chunks w, w + 4, ..., each wave staging its chunk's codes and scales
-// in two LDS stages of its own (one in flight) and widening them itself into
-// its own bf16 chunk, so no barrier is needed until the states are merged.
+// in two LDS stages of its own (one in flight), so no barrier is needed until
+// the states are merged.  The codes are widened to bf16 in registers on their
+// way to the matrix cores: the K operand (8 channels of a key) is an 8-byte
+// read of a code row, the V^T operand (8 keys of a channel) an 8-bit
+// transposed read (ds_read_b64_tr_b8: in each 16-lane group, byte b of lane i
+// comes from byte i % 8 of the row lane 2b + i / 8 points at).  The copies
+// swizzle each code row's 16-byte chunks so that both reads spread over the
+// LDS banks; the scales are read raw and the ones past the context replaced
+// by 0 in registers.
 constexpr int kI8FewKeys = 32;
 template <int D>
 __global__ __launch_bounds__(256) void prefill_i8_few_rows_kernel(PrefillArgs a) {
   using Tl = PfTile<D>;
   constexpr int kCodes = kI8FewKeys * D;                       // codes of K (or V) of a chunk
   constexpr int kStage = 2 * kCodes + 2 * kI8FewKeys * 4;       // codes + raw K, V scales
-  constexpr int kChunkBf = 2 * kI8FewKeys * Tl::kRowBytes;      // bf16 K then V
-  constexpr int kWaveBytes = 2 * kStage + kChunkBf + 2 * kI8FewKeys * 4;
+  constexpr int kWaveBytes = 2 * kStage;
+  constexpr int kRowChunks = D / 16;                           // 16-byte chunks of a code row
+  constexpr int kRowsPerLine = 256 / D;                        // code rows per 64 LDS banks
   constexpr int NC = D / 16;
   constexpr int NT = D / 32;
   constexpr int kCopiesPerBlock = kBlock * D / 1024;
@@ -372,9 +380,8 @@ __global__ __launch_bounds__(256) void prefill_i8_few_rows_kernel(PrefillArgs a)
   const unsigned char* vs = reinterpret_cast<const unsigned char*>(a.v_scale);
   const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   unsigned char* const mine = lds + wave * kWaveBytes;
-  unsigned char* const cbf = mine + 2 * kStage;                          // bf16 chunk
-  float* const ksc = reinterpret_cast<float*>(cbf + kChunkBf);          // sanitised scales
-  float* const vsc = ksc + kI8FewKeys;
+  // Physical 16-byte chunk of logical chunk ch of code row r (an involution).
+  auto swz = [](int r, int ch) { return ch ^ ((r / kRowsPerLine) % kRowChunks); };
 
   // Raw table entry of block b (0 or 1) of chunk c, a scalar load; clamped
   // where it is used, so the load has an iteration to land.
@@ -394,7 +401,12 @@ __global__ __launch_bounds__(256) void prefill_i8_few_rows_kernel(PrefillArgs a)
       const size_t bh = (size_t)blk * a.h_kv + kvh;
 #pragma unroll
       for (int i = 0; i < kCopiesPerBlock; ++i) {
-        const size_t src = bh * (kBlock * D) + (size_t)i * 1024 + lane * 16;
+        // Lane l fills LDS bytes 16 l .. 16 l + 15 of this copy: row rb of
+        // the block, physical chunk pc, i.e. logical chunk swz(row, pc).
+        const int pos = i * 1024 + lane * 16;
+        const int rb = pos / D;
+        const int pc = (pos % D) / 16;
+        const size_t src = bh * (kBlock * D) + (size_t)rb * D + swz(b * kBlock + rb, pc) * 16;
         const int d = b * kBlock * D + i * 1024;
         copy_to_lds(kc + src, dst + d);
         copy_to_lds(vc + src, dst + kCodes + d);
@@ -405,36 +417,6 @@ __global__ __launch_bounds__(256) void prefill_i8_few_rows_kernel(PrefillArgs a)
       }
     }
   };
-  // Widens chunk c (stage st) into this wave's bf16 chunk and sanitised scales.
-  auto convert_chunk = [&](int c, int st) {
-    const unsigned char* src = mine + st * kStage;
-    const int valid = Lu - c * kI8FewKeys;
-    constexpr int kUnits = 2 * kI8FewKeys * Tl::kChunks;
-#pragma unroll
-    for (int u0 = 0; u0 < kUnits; u0 += 64) {
-      const int u = u0 + lane;
-      const int isv = u >= kI8FewKeys * Tl::kChunks;
-      const int uu = isv ? u - kI8FewKeys * Tl::kChunks : u;
-      const int row = uu / Tl::kChunks;
-      const int ch = uu - row * Tl::kChunks;
-      const uint2 w = *reinterpret_cast<const uint2*>(src + isv * kCodes + row * D + ch * 8);
-      uint4 x;
-      widen4(w.x, x.x, x.y);
-      widen4(w.y, x.z, x.w);
-      if (isv && row >= valid) x = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(cbf + isv * kI8FewKeys * Tl::kRowBytes + Tl::offset(row, ch)) = x;
-    }
-    {
-      const int key = lane & (kI8FewKeys - 1);
-      const int isv = lane >= kI8FewKeys;
-      const float* raw = reinterpret_cast<const float*>(src + 2 * kCodes);
-      const float x = raw[(key >> 4) * 32 + isv * 16 + (key & 15)];
-      const float y = key < valid ? x : 0.f;
-      (isv ? vsc : ksc)[key] = isv ? y : y * csc;
-    }
-    wait_lds();
-  };
-
   bf16x8_t qb[NC];
   {
     const uint4* qv = reinterpret_cast<const uint4*>(a.q);
@@ -449,9 +431,14 @@ __global__ __launch_bounds__(256) void prefill_i8_few_rows_kernel(PrefillArgs a)
       qb[c] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
-  const int grp = lane >> 4;
-  const int tr_row = 4 * (grp >> 1) + ((lane & 15) >> 2);
-  const int tr_ch = 16 * (grp & 1) + 4 * (lane & 3);
+  // V^T operand addressing (see above): this lane points at key row
+  // 8 (b / 4) + 4 h + b % 4 (b = (lane % 16) / 2, h = lane / 32) of a 16-key
+  // half and at byte 8 (lane % 2) of the 16 channels of its 16-lane group, so
+  // that it receives the 8 keys of channel lane % 32 in the P^T operand's key
+  // order (accumulator element e: key 8 (e / 4) + 4 h + e % 4).
+  const int vt_b = (lane & 15) >> 1;
+  const int vt_row = 8 * (vt_b >> 2) + 4 * half + (vt_b & 3);
+  const int vt_ch = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
 
   if (wave < n_chunks) issue_chunk(0, entry(wave, 0), entry(wave, 1));
   // Entries of the chunk after next are requested an iteration before their
@@ -469,25 +456,40 @@ __global__ __launch_bounds__(256) void prefill_i8_few_rows_kernel(PrefillArgs a)
       wait_vm<kCopies>();
     else
       wait_vm<0>();
-    convert_chunk(c, st);
+    const unsigned char* kb = mine + st * kStage;
+    const unsigned char* vb = kb + kCodes;
+    const float* raw = reinterpret_cast<const float*>(kb + 2 * kCodes);
     const int key0 = c * kI8FewKeys;
+    const int valid = Lu - key0;
     f32x16_t sc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[i] = 0.f;
 #pragma unroll
     for (int c2 = 0; c2 < NC; ++c2) {
-      const uint4 kx = *reinterpret_cast<const uint4*>(cbf + Tl::offset(col, 2 * c2 + half));
+      // Channels 16 c2 + 8 half .. + 7 of key col: half of logical chunk c2.
+      const uint2 w = *reinterpret_cast<const uint2*>(kb + col * D + swz(col, c2) * 16 + 8 * half);
+      uint4 kx;
+      widen4(w.x, kx.x, kx.y);
+      widen4(w.y, kx.z, kx.w);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx), qb[c2], sc, 0,
                                                    0, 0);
     }
-    // Keys of accumulator elements 4j .. 4j + 3: 8 j + 4 half + 0..3.
+    // Keys of accumulator elements 4j .. 4j + 3: 8 j + 4 half + 0..3, in block
+    // j / 2; raw scales of block b at floats 32 b (K) and 32 b + 16 (V).  A slot
+    // past the context may hold anything (NaN included): selected away.
     float kf[16], vf[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float4 k4 = *reinterpret_cast<const float4*>(ksc + 8 * j + 4 * half);
-      const float4 v4 = *reinterpret_cast<const float4*>(vsc + 8 * j + 4 * half);
-      kf[4 * j + 0] = k4.x; kf[4 * j + 1] = k4.y; kf[4 * j + 2] = k4.z; kf[4 * j + 3] = k4.w;
-      vf[4 * j + 0] = v4.x; vf[4 * j + 1] = v4.y; vf[4 * j + 2] = v4.z; vf[4 * j + 3] = v4.w;
+      const int key = 8 * j + 4 * half;
+      const float4 k4 = *reinterpret_cast<const float4*>(raw + (key >> 4) * 32 + (key & 15));
+      const float4 v4 = *reinterpret_cast<const float4*>(raw + (key >> 4) * 32 + 16 + (key & 15));
+      const float kr[4] = {k4.x, k4.y, k4.z, k4.w};
+      const float vr[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf[4 * j + e] = key + e < valid ? kr[e] * csc : 0.f;
+        vf[4 * j + e] = key + e < valid ? vr[e] : 0.f;
+      }
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[i] *= kf[i];
@@ -520,7 +522,6 @@ __global__ __launch_bounds__(256) void prefill_i8_few_rows_kernel(PrefillArgs a)
       sc[i] = p * vf[i];
     }
     lsum += ps;
-    const unsigned char* vb = cbf + kI8FewKeys * Tl::kRowBytes;
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       uint4 pw;
@@ -529,21 +530,21 @@ __global__ __launch_bounds__(256) void prefill_i8_few_rows_kernel(PrefillArgs a)
       pw.z = pack_bf16x2(sc[8 * c2 + 4], sc[8 * c2 + 5]);
       pw.w = pack_bf16x2(sc[8 * c2 + 6], sc[8 * c2 + 7]);
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+      const int vr = 16 * c2 + vt_row;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const int chn = 32 * t + tr_ch;
-        const int ra = 16 * c2 + tr_row;
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (PKV_LDS i16x4_t*)(vb + Tl::offset(ra, chn >> 3) + (chn & 4) * 2));
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (PKV_LDS i16x4_t*)(vb + Tl::offset(ra + 8, chn >> 3) + (chn & 4) * 2));
-        const i16x4_t lohi[2] = {lo, hi};
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lohi), pb, o[t],
+        const int ch = 32 * t + vt_ch;
+        const i32x2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (PKV_LDS i32x2_t*)(vb + vr * D + swz(vr, ch >> 4) * 16 + (ch & 8)));
+        uint4 vx;
+        widen4((uint32_t)w[0], vx.x, vx.y);
+        widen4((uint32_t)w[1], vx.z, vx.w);
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vx), pb, o[t],
                                                        0, 0, 0);
       }
     }
-    // The bf16 chunk and the stage are rewritten only after every read of
-    // this iteration has returned.
+    // The stage is rewritten only after every read of this iteration has
+    // returned.
     wait_lds();
   }
 

@@ -324,8 +324,10 @@ __global__ __launch_bounds__(256) void prefill_i8_kernel(PrefillArgs a) {
 // LDS banks; the scales are read raw and the ones past the context replaced
 // by 0 in registers.
 constexpr int kI8FewKeys = 32;
+// Two workgroups per compute unit (at most 256 VGPRs: two waves per SIMD; the
+// stages take 66 KiB of LDS at d_h = 128).
 template <int D>
-__global__ __launch_bounds__(256) void prefill_i8_few_rows_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_i8_few_rows_kernel(PrefillArgs a) {
   using Tl = PfTile<D>;
   constexpr int kCodes = kI8FewKeys * D;                       // codes of K (or V) of a chunk
   constexpr int kStage = 2 * kCodes + 2 * kI8FewKeys * 4;       // codes + raw K, V scales

@@ -129,9 +129,11 @@ int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
  *                  matter.  The caller owns it and must not use it
  *                  concurrently with the call.
  * The blocks of all (sequence, KV head) pairs, laid end to end, are cut into
- * one range per wavefront the device holds at once (ranges of wavefronts on
- * even XCDs 11/10 the size of those on odd XCDs, which run slower); results
- * do not depend on the cut beyond fp32 rounding.  B == 0 enqueues nothing.
+ * one range per wavefront the device holds at once, or fewer where the line
+ * is short (at most one range per two blocks of the longest line the
+ * arguments allow); ranges of wavefronts on even XCDs are 11/10 the size of
+ * those on odd XCDs, which run slower.  Results do not depend on the cut
+ * beyond fp32 rounding.  B == 0 enqueues nothing.
  * Requires h_q % h_kv == 0, d_h in {64, 128}; returns PKV_ERR_UNSUPPORTED
  * when B * h_kv * ceil(max_context_len / 16) exceeds 2^40 block reads.
  */

@@ -665,31 +665,26 @@ __device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int b) {
   return (seq_len(a, b) + kBlock - 1) / kBlock;
 }
 
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+// Inclusive prefix sum over the wave's lanes (64-bit: 64 rows of up to 2^27
+// blocks each can pass 2^31).
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t x, int lane) {
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o);
+    const int64_t y = __shfl_up(x, o);
     if (lane >= o) x += y;
   }
   return x;
 }
 
-// Blocks of all sequences before b (if b >= 0) and of all sequences.
-struct ScanResult {
-  int64_t before;
-  int64_t total;
-};
-__device__ __forceinline__ ScanResult scan_blocks(const DecodeArgs& a, int b, int lane) {
-  ScanResult r{0, 0};
+// Blocks of all sequences, read in chunks of 64 sequences (one per lane).
+__device__ __forceinline__ int64_t total_blocks(const DecodeArgs& a, int lane) {
+  int64_t total = 0;
   for (int c0 = 0; c0 < a.B; c0 += kWave) {
     const int bb = c0 + lane;
-    const int n = bb < a.B ? seq_blocks(a, bb) : 0;
-    const int incl = wave_incl_scan(n, lane);
-    const int chunk_total = uniform(__shfl(incl, kWave - 1));
-    if (b >= c0 && b < c0 + kWave) r.before = r.total + __shfl(incl, b - c0) - __shfl(n, b - c0);
-    r.total += chunk_total;
+    const int64_t incl = wave_incl_scan(bb < a.B ? seq_blocks(a, bb) : 0, lane);
+    total += uniform((int64_t)__shfl(incl, kWave - 1));
   }
-  return r;
+  return total;
 }
 
 // Merges the partial states of head j of one segment cut by range boundaries
@@ -1083,15 +1078,27 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void decode_split_kernel(Decod
   if ((int)blockIdx.x >= (a.num_splits + kSplitWaves - 1) / kSplitWaves / 2)
     __builtin_amdgcn_s_setprio(2);
 
+  // Context lengths.  A batch of at most 64 sequences is read once, one
+  // sequence per lane, and the zero-length outputs, the line length and the
+  // search for the wave's first piece all take their lengths from that one
+  // load instead of waiting for three loads in turn (about one memory round
+  // trip less before the first block is requested).  Larger batches are read
+  // in chunks of 64 sequences for each.
+  const bool one_load = a.B <= kWave;
+  const int len_lane = (one_load && lane < a.B) ? seq_len(a, lane) : 0;
+  const int n_lane = (len_lane + kBlock - 1) / kBlock;
+  const int64_t incl_lane = wave_incl_scan(n_lane, lane);
+
   // Sequences of length 0 get an all-zero output (sequence b by wave b mod splits).
   for (int b0 = W; in_grid && b0 < a.B; b0 += a.num_splits) {
-    if (seq_len(a, b0) != 0) continue;
+    if ((one_load ? __builtin_amdgcn_readlane(len_lane, b0) : seq_len(a, b0)) != 0) continue;
     OutOf<T>* out = reinterpret_cast<OutOf<T>*>(a.out) + (size_t)b0 * a.h_q * D;
     for (int i = lane; i < a.h_q * D; i += kWave) store_elem<OutOf<T>>(out, i, 0.f);
   }
 
-  const ScanResult all = scan_blocks(a, -1, lane);
-  const Line line{all.total * HC, a.num_splits};
+  const int64_t total =
+      one_load ? uniform((int64_t)__shfl(incl_lane, kWave - 1)) : total_blocks(a, lane);
+  const Line line{total * HC, a.num_splits};
   if (W == 0 && lane == 0) *a.line_total = line.total;  // for the second pass
   if (line.total == 0 || !in_grid) return;
   const int64_t s = line.start(W);
@@ -1106,8 +1113,8 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void decode_split_kernel(Decod
     int64_t seq0 = 0;
     for (int c0 = 0; c0 < a.B; c0 += kWave) {
       const int bb = c0 + lane;
-      const int n = bb < a.B ? seq_blocks(a, bb) : 0;
-      const int incl = wave_incl_scan(n, lane);
+      const int n = one_load ? n_lane : (bb < a.B ? seq_blocks(a, bb) : 0);
+      const int64_t incl = one_load ? incl_lane : wave_incl_scan(n, lane);
       const uint64_t hit = __ballot(bb < a.B && (base + incl) * HC > s);
       if (hit) {
         const int f = __builtin_ctzll(hit);

@@ -260,6 +260,29 @@ def kv_append_int8(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch
         raise PkvError("kv_append_int8", rc)
 
 
+def bind_kv_append_int8(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                        k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                        v_scale: torch.Tensor):
+    """kv_append_int8 with its arguments checked and marshalled once: returns a
+    call that launches it (on the stream current now)."""
+    kv_append_int8(k_new[:0], v_new[:0], slot_mapping[:0], k_cache, v_cache, k_scale,
+                   v_scale)   # the checks
+    n_blocks, h_kv, d = _pool_shape(k_cache, v_cache)
+    _need(k_new.shape[0] == slot_mapping.shape[0] and v_new.shape == k_new.shape,
+          "k_new/v_new/slot_mapping lengths differ")
+    _need(k_new.is_contiguous() and v_new.is_contiguous(), "k_new/v_new must be contiguous")
+    fn = lib().kv_append_int8
+    args = (k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
+            v_cache.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(), int(k_new.shape[0]),
+            h_kv, d, n_blocks, _DTYPE[k_new.dtype], _stream(k_cache))
+
+    def call() -> None:
+        rc = fn(*args)
+        if rc != 0:
+            raise PkvError("kv_append_int8", rc)
+    return call
+
+
 def paged_decode_attention_int8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                 k_scale: torch.Tensor, v_scale: torch.Tensor,
                                 block_tables: torch.Tensor, context_lens: torch.Tensor,
@@ -297,6 +320,36 @@ def paged_decode_attention_int8(q: torch.Tensor, k_cache: torch.Tensor, v_cache:
     if rc != 0:
         raise PkvError("paged_decode_attention_int8", rc)
     return out
+
+
+def bind_decode_int8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     k_scale: torch.Tensor, v_scale: torch.Tensor, block_tables: torch.Tensor,
+                     context_lens: torch.Tensor, max_context_len: int, out: torch.Tensor,
+                     workspace: torch.Tensor, scale: Optional[float] = None,
+                     num_splits: int = 0):
+    """paged_decode_attention_int8 with its arguments checked and marshalled
+    once (the first launch runs through the checked call): returns a call that
+    launches it again on the same buffers (on the stream current now)."""
+    paged_decode_attention_int8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                context_lens, max_context_len, scale=scale,
+                                num_splits=num_splits, out=out, workspace=workspace)
+    n_blocks, h_kv, d = _pool_shape(k_cache, v_cache)
+    B, h_q = int(q.shape[0]), int(q.shape[1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    fn = lib().paged_decode_attention_int8
+    args = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            k_scale.data_ptr(), v_scale.data_ptr(), block_tables.data_ptr(),
+            context_lens.data_ptr(), B, h_q, h_kv, d, n_blocks, int(block_tables.shape[1]),
+            int(max_context_len), float(scale), int(num_splits), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream(q))
+
+    def call() -> torch.Tensor:
+        rc = fn(*args)
+        if rc != 0:
+            raise PkvError("paged_decode_attention_int8", rc)
+        return out
+    return call
 
 
 def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -7,16 +7,19 @@
 // Attention Kernel box of the pipeline figure, From Scratch page).
 //
 // Design: the bf16 prefill's tiling and matrix products (prefill.hip: GQA rows
-// packed, 128 rows per workgroup of 4 waves, 64-key tiles, S^T = K Q^T and
-// O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, lazy-rescale online softmax),
-// with the cache read as codes:
+// packed, 128 rows per workgroup of 4 waves, at d_h = 64 two such groups over
+// alternate key tiles when the grid fits the chip, 64-key tiles, S^T = K Q^T
+// and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, lazy-rescale online
+// softmax), with the cache read as codes:
 //  * the codes and scales of a tile (half the bytes of a bf16 tile) are copied
 //    straight from HBM into one of three LDS staging buffers, two tiles ahead;
-//  * all 256 threads widen the tile's codes exactly to bf16 (|c| <= 127 needs
-//    8 significant bits) into the swizzled bf16 tile layout the matrix reads
-//    use, once per workgroup, and write the tile's scales with the keys past
-//    the context set to 0 (their slots may hold anything) and the K scales
-//    multiplied by |scale| * log2(e);
+//  * the 256 threads of a group widen the tile's codes exactly to bf16
+//    (|c| <= 127 needs 8 significant bits) into the swizzled bf16 tile layout
+//    the matrix reads use, once per group, and write the tile's scales with
+//    the keys past the context set to 0 (their slots may hold anything) and
+//    the K scales multiplied by |scale| * log2(e).  (Widening in registers as
+//    each wave reads its operands, as the few-rows kernel below does, repeats
+//    the work in every row wave: 4 x 4096-token prompts took 17-25% longer.)
 //  * the K scale multiplies each score S^T (one key per accumulator element);
 //    the V scale multiplies each softmax weight before it is rounded to bf16
 //    for the P^T operand (the normaliser sums the unscaled weights), so
@@ -51,17 +54,20 @@ struct I8Stage {
 
 }  // namespace
 
-template <int D>
-__global__ __launch_bounds__(256) void prefill_i8_kernel(PrefillArgs a) {
+// KS groups of 4 waves share a workgroup's 128 rows and split its key tiles,
+// as in the bf16 prefill: group G takes tiles G, G + KS, ..., each group with
+// its own staging buffers, bf16 tile and scales, and the groups' softmax
+// states are merged at the end.  KS = 2 halves the serial key walk of the
+// longest rows when the grid alone cannot fill the chip.
+template <int D, int KS>
+__global__ __launch_bounds__(256 * KS) void prefill_i8_kernel(PrefillArgs a) {
   using Tl = PfTile<D>;
   using St = I8Stage<D>;
-  // LDS: three staging buffers (codes of K and V, raw K and V scales), one
-  // bf16 tile (K then V), and the tile's sanitised scales (K, then V).
-  __shared__ __attribute__((aligned(16))) unsigned char lds[3 * St::kBytes + 2 * Tl::kMatBytes +
-                                                            2 * kPfTile * 4];
-  unsigned char* const tile = lds + 3 * St::kBytes;
-  float* const ksc = reinterpret_cast<float*>(tile + 2 * Tl::kMatBytes);
-  float* const vsc = ksc + kPfTile;
+  // LDS per group: three staging buffers (codes of K and V, raw K and V
+  // scales), one bf16 tile (K then V), and the tile's sanitised scales (K,
+  // then V).
+  constexpr int kGroupBytes = 3 * St::kBytes + 2 * Tl::kMatBytes + 2 * kPfTile * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[KS * kGroupBytes];
   constexpr int NC = D / 16;
   constexpr int NT = D / 32;
   // copies per wave per tile: its block's K and V codes, plus one for the scales
@@ -80,8 +86,10 @@ __global__ __launch_bounds__(256) void prefill_i8_kernel(PrefillArgs a) {
   if (n <= 0 || n > L || r0 >= rows || q0 < 0 || q0 + n > a.T_q) return;
 
   const int tid = threadIdx.x;
+  const int gtid = tid & 255;  // thread index within the group
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // row wave in the group
+  const int grp_id = __builtin_amdgcn_readfirstlane(tid >> 8);       // key-split group
   const int col = lane & 31;
   const int half = lane >> 5;
   const int first = L - n;
@@ -97,7 +105,12 @@ __global__ __launch_bounds__(256) void prefill_i8_kernel(PrefillArgs a) {
   const int wave_pos_hi = first + (min(wave_r0 + 31, rows - 1)) / g;
   const int wg_pos_hi = first + (min(r0 + kPfRows - 1, rows - 1)) / g;
   const int n_tiles = __builtin_amdgcn_readfirstlane(wg_pos_hi / kPfTile + 1);
+  const int n_steps = (n_tiles + KS - 1) / KS;  // tiles per group, rounded up
   const int Lu = __builtin_amdgcn_readfirstlane(L);
+  unsigned char* const glds = lds + grp_id * kGroupBytes;
+  unsigned char* const tile = glds + 3 * St::kBytes;
+  float* const ksc = reinterpret_cast<float*>(tile + 2 * Tl::kMatBytes);
+  float* const vsc = ksc + kPfTile;
 
   const float csc = fabsf(a.scale_log2);
   const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
@@ -114,22 +127,23 @@ __global__ __launch_bounds__(256) void prefill_i8_kernel(PrefillArgs a) {
   const unsigned char* ks = reinterpret_cast<const unsigned char*>(a.k_scale);
   const unsigned char* vs = reinterpret_cast<const unsigned char*>(a.v_scale);
   const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks_per_seq;
-  auto stage = [&](int kt) { return lds + (kt % 3) * St::kBytes; };
+  // The group's i-th tile is staged in its buffer i % 3.
+  auto stage = [&](int i) { return glds + (i % 3) * St::kBytes; };
 
-  // Copies block (4 * kt + wave) of tile kt into its staging buffer: the K and
-  // V codes of that block (rows 16 * wave ..), and its 16 K and 16 V scales
-  // (lanes 0-3 and 4-7 of one more copy) into the scale area (wave w's block
-  // at floats 32 w .. 32 w + 31: K then V).
-  auto issue_tile = [&](int kt) {
+  // Copies block (4 * kt + wave) of tile kt, the group's i-th, into its
+  // staging buffer: the K and V codes of that block (rows 16 * wave ..), and
+  // its 16 K and 16 V scales (lanes 0-3 and 4-7 of one more copy) into the
+  // scale area (wave w's block at floats 32 w .. 32 w + 31: K then V).
+  auto issue_tile = [&](int kt, int i) {
     const int bi = min(kt * (kPfTile / kBlock) + wave, a.max_blocks_per_seq - 1);
     int blk = constant_view(trow)[bi];
     blk = (blk >= 0 && blk < a.n_blocks) ? blk : 0;
     const size_t bh = (size_t)blk * a.h_kv + kvh;
-    unsigned char* st = stage(kt);
+    unsigned char* st = stage(i);
 #pragma unroll
-    for (int i = 0; i < St::kCopiesPerBlock; ++i) {
-      const size_t src = bh * (kBlock * D) + (size_t)i * 1024 + lane * 16;
-      const int dst = wave * kBlock * D + i * 1024;
+    for (int c = 0; c < St::kCopiesPerBlock; ++c) {
+      const size_t src = bh * (kBlock * D) + (size_t)c * 1024 + lane * 16;
+      const int dst = wave * kBlock * D + c * 1024;
       copy_to_lds(kc + src, st + dst);
       copy_to_lds(vc + src, st + St::kCodeMat + dst);
     }
@@ -139,16 +153,16 @@ __global__ __launch_bounds__(256) void prefill_i8_kernel(PrefillArgs a) {
     }
   };
 
-  // Widens tile kt's codes (staged) into the bf16 tile and writes its
-  // sanitised scales (all threads).  Rows past the context: V zero, both
-  // scales zero.
-  auto convert_tile = [&](int kt) {
-    const unsigned char* st = stage(kt);
+  // Widens tile kt's codes (staged as the group's i-th tile) into the group's
+  // bf16 tile and writes its sanitised scales (the group's 256 threads).  Rows
+  // past the context: V zero, both scales zero.
+  auto convert_tile = [&](int kt, int i) {
+    const unsigned char* st = stage(i);
     const int valid = Lu - kt * kPfTile;  // rows of this tile inside the context
     constexpr int kUnits = 2 * kPfTile * Tl::kChunks;  // 8-code units of K and V
 #pragma unroll
     for (int u0 = 0; u0 < kUnits; u0 += 256) {
-      const int u = u0 + tid;
+      const int u = u0 + gtid;
       const int isv = u >= kPfTile * Tl::kChunks;
       const int uu = isv ? u - kPfTile * Tl::kChunks : u;
       const int row = uu / Tl::kChunks;
@@ -160,9 +174,9 @@ __global__ __launch_bounds__(256) void prefill_i8_kernel(PrefillArgs a) {
       if (isv && row >= valid) x = make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(tile + isv * Tl::kMatBytes + Tl::offset(row, ch)) = x;
     }
-    if (tid < 2 * kPfTile) {
-      const int key = tid & (kPfTile - 1);
-      const int isv = tid >= kPfTile;
+    if (gtid < 2 * kPfTile) {
+      const int key = gtid & (kPfTile - 1);
+      const int isv = gtid >= kPfTile;
       const float* raw = reinterpret_cast<const float*>(st + 2 * St::kCodeMat);
       // raw layout: block w = key / 16 at floats 32 w (K) and 32 w + 16 (V)
       const float x = raw[(key >> 4) * 32 + isv * 16 + (key & 15)];
@@ -189,21 +203,26 @@ __global__ __launch_bounds__(256) void prefill_i8_kernel(PrefillArgs a) {
       qb[c] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
-  issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
+  if (grp_id < n_tiles) issue_tile(grp_id, 0);
+  if (grp_id + KS < n_tiles) issue_tile(grp_id + KS, 1);
   wait_vm<0>();
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    // Tile kt's copies landed (own ones: all but tile kt + 1's), then every
-    // wave's (barrier); every wave is also done with tile kt - 1.
-    if (kt + 1 < n_tiles) wait_vm<kCopies>();
+  // Step i: every group converts and attends its i-th tile, tile kt = i * KS +
+  // group; all groups pass the same barriers.
+  for (int i = 0; i < n_steps; ++i) {
+    const int kt = i * KS + grp_id;
+    const bool mine = kt < n_tiles;
+    // Tile kt's copies landed (own ones: all but the group's next tile's),
+    // then every wave's (barrier); every wave is also done with its previous
+    // tile.
+    if (mine && kt + KS < n_tiles) wait_vm<kCopies>();
     else wait_vm<0>();
     tile_barrier();
-    convert_tile(kt);
+    if (mine) convert_tile(kt, i);
     wait_lds();
     tile_barrier();
-    if (kt + 2 < n_tiles) issue_tile(kt + 2);
-    if (!(wave_live && kt * kPfTile <= wave_pos_hi)) continue;
+    if (mine && kt + 2 * KS < n_tiles) issue_tile(kt + 2 * KS, i + 2);
+    if (!(mine && wave_live && kt * kPfTile <= wave_pos_hi)) continue;
 
     const int key0 = kt * kPfTile;
     f32x16_t sc[2];
@@ -292,6 +311,37 @@ __global__ __launch_bounds__(256) void prefill_i8_kernel(PrefillArgs a) {
                                                        0, 0, 0);
       }
     }
+  }
+
+  if constexpr (KS == 2) {
+    // Group 1 hands its state for the same rows to group 0 through LDS (field
+    // f of lane l of row wave w at float (f * 4 + w) * 64 + l), which merges
+    // the two with the log-sum-exp rule.
+    constexpr int kFields = NT * 16 + 2;
+    static_assert(kFields * 4 * 64 * 4 <= (int)sizeof(lds), "merge area");
+    float* mg = reinterpret_cast<float*>(lds);
+    auto at = [&](int f) -> float& { return mg[(f * 4 + wave) * 64 + lane]; };
+    tile_barrier();  // every wave is done with the tiles
+    if (grp_id == 1) {
+      at(0) = m;
+      at(1) = lsum;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) at(2 + t * 16 + e) = o[t][e];
+    }
+    wait_lds();
+    tile_barrier();
+    if (grp_id == 1) return;
+    const float m1 = at(0);
+    const float mm = fmaxf(m, m1);
+    const float a0 = m == kPfNegInf ? 0.f : fast_exp2(m - mm);
+    const float a1 = m1 == kPfNegInf ? 0.f : fast_exp2(m1 - mm);
+    lsum = lsum * a0 + at(1) * a1;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[t][e] = o[t][e] * a0 + at(2 + t * 16 + e) * a1;
   }
 
   if (!row_ok) return;
@@ -626,7 +676,16 @@ static hipError_t launch_i8_d(const PrefillArgs& a, hipStream_t stream) {
   // Sequence planes longest context first when the grid takes more than one
   // round of the chip (as for the bf16 prefill).
   args.longest_first = a.S > 1 && a.S <= kLptMaxSeqs && cus > 0 && gx * a.h_kv * a.S > cus;
-  hipLaunchKernelGGL((prefill_i8_kernel<D>), grid, dim3(256), 0, stream, args);
+  // Split the key walk over two wave groups when the grid has no more
+  // workgroups than the chip has compute units (d_h = 64, as for the bf16
+  // prefill).
+  if constexpr (D == 64) {
+    if (cus > 0 && gx * a.h_kv * a.S <= cus) {
+      hipLaunchKernelGGL((prefill_i8_kernel<D, 2>), grid, dim3(512), 0, stream, args);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((prefill_i8_kernel<D, 1>), grid, dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 

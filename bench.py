@@ -363,18 +363,19 @@ def time_long_prefill(dev: str, iters: int = 5, warmup: int = 30, batches: int =
 def time_int8_prefill(dev: str, w5: W.Workload, iters: int):
     """paged_prefill_attention_int8: config 5's 4 prompts of 512 tokens over an
     INT8 cache of the same shape (random codes and scales), and the 4-token
-    verify of the decode batch's 64 sequences over an INT8 cache; back-to-back
-    calls through bound launches."""
+    verify of the decode batch's 64 sequences over an INT8 cache; each the
+    median of 5 batches of back-to-back calls through bound launches."""
     res = {}
     pi = W.int8_pools(w5, seed=50)
     p8 = [t.to(dev) for t in (pi.k_codes, pi.v_codes, pi.k_scales, pi.v_scales)]
     q, cu = w5.pre_q.to(dev), w5.pre_cu_seqlens.to(dev)
     call = ops.bind_prefill_int8(q, cu, *p8, w5.pre_block_tables.to(dev),
                                  w5.pre_context_lens.to(dev), w5.pre_max_q_len, scale=w5.scale)
-    ms = time_calls(lambda i: call(), iters, warmup=5)
+    ms, per = time_batches(lambda i: call(), max(iters, 20))
     fl = prefill_flops(w5)
     res["prompts"] = {"workload": "4 prompts x 512 tokens, h_q=14, h_kv=2, d_h=64, causal, "
                                   "INT8 cache", "flops": fl, "avg_us": round(ms * 1e3, 2),
+                      "batches_us": [round(x * 1e3, 2) for x in per],
                       "tflops": round(fl / (ms / 1e3) / 1e12, 2)}
     del p8, call
     wk = W.config(3)

@@ -203,6 +203,27 @@ def test_workspace_bound(B, h_q, h_kv, d, maxc, dtype):
     assert ops.decode_num_splits(B, h_q, h_kv, d, maxc, dtype, num_splits=48) == 48
 
 
+@pytest.mark.parametrize("B,h_q,h_kv,d,maxc,dtype,half_line", [
+    (8, 32, 8, 64, 512, torch.bfloat16, 1024),    # 8 x 512 tokens at 32/8/64: 2048 block reads
+    (2, 4, 2, 64, 40, torch.float32, 6),         # 2 x 40 tokens at 4/2/64: 12 block reads
+    (1, 1, 1, 64, 16, torch.bfloat16, 1),        # one block
+    (64, 32, 8, 128, 4096, torch.bfloat16, None),  # a long line: one range per resident wave
+])
+def test_automatic_split_count_is_capped_by_the_line(B, h_q, h_kv, d, maxc, dtype, half_line):
+    """The automatic split count never exceeds half the blocks of the longest
+    line the arguments allow (rounded up), so no short line is cut into
+    one-block pieces; a long line keeps one range per resident wavefront."""
+    n = ops.decode_num_splits(B, h_q, h_kv, d, maxc, dtype)
+    assert n >= 1
+    if half_line is not None:
+        assert n <= half_line
+    else:
+        assert 256 <= n <= 4096
+    # the workspace of the automatic split holds that many ranges
+    assert ops.decode_workspace_bytes(B, h_q, h_kv, d, maxc, dtype) >= \
+        ops.decode_workspace_bytes(B, h_q, h_kv, d, maxc, dtype, n)
+
+
 def _append8(**kw):
     a = dict(k_new=FAKE, v_new=FAKE, slots=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, T=4, h_kv=2,
              d=64, nb=8, dt=1)

@@ -63,3 +63,26 @@ def test_invalid_arguments():
     assert wave_of(10, 4, 10) == -1
     assert wave_of(10, 4, -1) == -1
     assert wave_of(0, 4, 0) == -1
+
+
+def _cum(u):
+    # weight of waves 0 .. u - 1: 11 for each wave of an even XCD, 10 for an odd one
+    r = u % 8
+    return (u // 8) * 84 + (r * 11 if r < 4 else 44 + (r - 4) * 10)
+
+
+@pytest.mark.parametrize("splits", [2048, 1000, 37])
+def test_exact_cut(splits):
+    """The cut and its inverse equal the exact integer formulas (start(w) =
+    floor(total * cum(w) / cum(splits)); the owner of p is the first wave
+    whose cumulative weight reaches ceil((p + 1) * cum(splits) / total)),
+    for lines whose products fit 32 bits and for longer ones."""
+    den = _cum(splits)
+    edge = (2 ** 32 - 1) // (den + 1)
+    for total in (edge - 1, edge, edge + 1, 77500, 5 * 10 ** 9):
+        cut = _cut(total, splits)
+        assert cut == [total * _cum(w) // den for w in range(splits + 1)], total
+        for p in (0, 1, total // 7, total // 2, total - 1) + tuple(cut[1:splits:97]):
+            t = -(-((p + 1) * den) // total)        # ceil((p + 1) * den / total)
+            w = min(u for u in range(splits + 1) if _cum(u + 1) >= t)
+            assert wave_of(total, splits, p) == w, (total, p)

@@ -38,6 +38,9 @@ Printed as one JSON line:
              decode batch (a speculative verify step), in KV GB/s; median of 5
              batches of back-to-back calls after 30 warm-up calls, like the
              INT8 verify
+  append     kv_append of the step's new tokens: HIP events around each call
+             inside the K steps (avg_us; includes the gap to the launch around
+             it) and back-to-back bound calls (back_to_back_us)
   int8_decode  paged_decode_attention_int8 on the same decode step over an
              INT8 cache: bytes = sum_b L_b * 2 * h_kv * (d_h + 4) (codes and
              one float32 scale per token head row), time over back-to-back
@@ -874,6 +877,7 @@ def main(argv=None):
     value = kvb * args.steps / wall / 1e9
     dec_avg_s = dec_med_ms / 1e3
     app_ms, dec_ms = time_step_parts(rk, args.steps)
+    app_b2b_ms = time_calls(rk.append, max(args.steps, 20), warmup=20)
     progress("decode roofline leg")
     achieved = kvb / dec_avg_s / 1e9
     app_bytes = 2 * wk.T * wk.h_kv * wk.d * wk.elem_bytes * 2 + wk.T * 8
@@ -1011,6 +1015,7 @@ def main(argv=None):
             "bytes": app_bytes,
             "avg_us": round(statistics.mean(app_ms) * 1e3, 2),
             "GBps": round(app_bytes / (statistics.mean(app_ms) / 1e3) / 1e9, 1),
+            "back_to_back_us": round(app_b2b_ms * 1e3, 2),
         },
         "long_context": None if args.config != 3 else {
             "workload": WORKLOAD[4],

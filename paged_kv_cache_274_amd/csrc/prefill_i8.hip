@@ -12,14 +12,18 @@
 // and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, lazy-rescale online
 // softmax), with the cache read as codes:
 //  * the codes and scales of a tile (half the bytes of a bf16 tile) are copied
-//    straight from HBM into one of three LDS staging buffers, two tiles ahead;
+//    straight from HBM into one of four LDS staging buffers, three tiles
+//    ahead;
 //  * the 256 threads of a group widen the tile's codes exactly to bf16
-//    (|c| <= 127 needs 8 significant bits) into the swizzled bf16 tile layout
-//    the matrix reads use, once per group, and write the tile's scales with
-//    the keys past the context set to 0 (their slots may hold anything) and
-//    the K scales multiplied by |scale| * log2(e).  (Widening in registers as
-//    each wave reads its operands, as the few-rows kernel below does, repeats
-//    the work in every row wave: 4 x 4096-token prompts took 17-25% longer.)
+//    (|c| <= 127 needs 8 significant bits) into one of two bf16 tiles in the
+//    swizzled layout the matrix reads use, once per group, and write the
+//    tile's scales with the keys past the context set to 0 (their slots may
+//    hold anything) and the K scales multiplied by |scale| * log2(e).  A
+//    wave widens the group's next tile right after attending the current
+//    one, so one barrier per step publishes both the copies and the widening.
+//    (Widening in registers as each wave reads its operands, as the few-rows
+//    kernel below does, repeats the work in every row wave: 4 x 4096-token
+//    prompts took 17-25% longer.)
 //  * the K scale multiplies each score S^T (one key per accumulator element);
 //    the V scale multiplies each softmax weight before it is rounded to bf16
 //    for the P^T operand (the normaliser sums the unscaled weights), so
@@ -63,10 +67,11 @@ template <int D, int KS>
 __global__ __launch_bounds__(256 * KS) void prefill_i8_kernel(PrefillArgs a) {
   using Tl = PfTile<D>;
   using St = I8Stage<D>;
-  // LDS per group: three staging buffers (codes of K and V, raw K and V
-  // scales), one bf16 tile (K then V), and the tile's sanitised scales (K,
-  // then V).
-  constexpr int kGroupBytes = 3 * St::kBytes + 2 * Tl::kMatBytes + 2 * kPfTile * 4;
+  // LDS per group: four staging buffers (codes of K and V, raw K and V
+  // scales) and two bf16 tiles (K then V), each with the tile's sanitised
+  // scales (K, then V).
+  constexpr int kBfBytes = 2 * Tl::kMatBytes + 2 * kPfTile * 4;
+  constexpr int kGroupBytes = 4 * St::kBytes + 2 * kBfBytes;
   __shared__ __attribute__((aligned(16))) unsigned char lds[KS * kGroupBytes];
   constexpr int NC = D / 16;
   constexpr int NT = D / 32;
@@ -108,9 +113,9 @@ __global__ __launch_bounds__(256 * KS) void prefill_i8_kernel(PrefillArgs a) {
   const int n_steps = (n_tiles + KS - 1) / KS;  // tiles per group, rounded up
   const int Lu = __builtin_amdgcn_readfirstlane(L);
   unsigned char* const glds = lds + grp_id * kGroupBytes;
-  unsigned char* const tile = glds + 3 * St::kBytes;
-  float* const ksc = reinterpret_cast<float*>(tile + 2 * Tl::kMatBytes);
-  float* const vsc = ksc + kPfTile;
+  // The group's i-th tile: codes in staging buffer i % 4, widened into bf16
+  // tile i % 2.
+  auto btile = [&](int i) { return glds + 4 * St::kBytes + (i & 1) * kBfBytes; };
 
   const float csc = fabsf(a.scale_log2);
   const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
@@ -127,8 +132,7 @@ __global__ __launch_bounds__(256 * KS) void prefill_i8_kernel(PrefillArgs a) {
   const unsigned char* ks = reinterpret_cast<const unsigned char*>(a.k_scale);
   const unsigned char* vs = reinterpret_cast<const unsigned char*>(a.v_scale);
   const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks_per_seq;
-  // The group's i-th tile is staged in its buffer i % 3.
-  auto stage = [&](int i) { return glds + (i % 3) * St::kBytes; };
+  auto stage = [&](int i) { return glds + (i & 3) * St::kBytes; };
 
   // Copies block (4 * kt + wave) of tile kt, the group's i-th, into its
   // staging buffer: the K and V codes of that block (rows 16 * wave ..), and
@@ -153,11 +157,14 @@ __global__ __launch_bounds__(256 * KS) void prefill_i8_kernel(PrefillArgs a) {
     }
   };
 
-  // Widens tile kt's codes (staged as the group's i-th tile) into the group's
-  // bf16 tile and writes its sanitised scales (the group's 256 threads).  Rows
-  // past the context: V zero, both scales zero.
+  // Widens tile kt's codes (staged as the group's i-th tile) into its bf16
+  // tile and writes its sanitised scales (the group's 256 threads).  Rows past
+  // the context: V zero, both scales zero.
   auto convert_tile = [&](int kt, int i) {
     const unsigned char* st = stage(i);
+    unsigned char* const tile = btile(i);
+    float* const ksc = reinterpret_cast<float*>(tile + 2 * Tl::kMatBytes);
+    float* const vsc = ksc + kPfTile;
     const int valid = Lu - kt * kPfTile;  // rows of this tile inside the context
     constexpr int kUnits = 2 * kPfTile * Tl::kChunks;  // 8-code units of K and V
 #pragma unroll
@@ -203,27 +210,34 @@ __global__ __launch_bounds__(256 * KS) void prefill_i8_kernel(PrefillArgs a) {
       qb[c] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
-  if (grp_id < n_tiles) issue_tile(grp_id, 0);
-  if (grp_id + KS < n_tiles) issue_tile(grp_id + KS, 1);
+  // Whether the group has an i-th tile.
+  auto has = [&](int i) { return i * KS + grp_id < n_tiles; };
+  if (has(0)) issue_tile(grp_id, 0);
+  if (has(1)) issue_tile(grp_id + KS, 1);
+  if (has(2)) issue_tile(grp_id + 2 * KS, 2);
   wait_vm<0>();
+  tile_barrier();
+  if (has(0)) convert_tile(grp_id, 0);
 
-  // Step i: every group converts and attends its i-th tile, tile kt = i * KS +
-  // group; all groups pass the same barriers.
+  // Step i: every group attends its i-th tile, tile kt = i * KS + group, and
+  // widens its next one, so one barrier per step separates each tile's
+  // widening from its use; all groups pass the same barriers.
   for (int i = 0; i < n_steps; ++i) {
     const int kt = i * KS + grp_id;
     const bool mine = kt < n_tiles;
-    // Tile kt's copies landed (own ones: all but the group's next tile's),
-    // then every wave's (barrier); every wave is also done with its previous
-    // tile.
-    if (mine && kt + KS < n_tiles) wait_vm<kCopies>();
+    // The group's next tile's copies have landed (own ones: all but the one
+    // after it) and this tile's widening is written (own writes), then every
+    // wave's (barrier); every wave is also done with the previous step's
+    // tile and with this tile's codes.
+    if (has(i + 2)) wait_vm<kCopies>();
     else wait_vm<0>();
-    tile_barrier();
-    if (mine) convert_tile(kt, i);
     wait_lds();
     tile_barrier();
-    if (mine && kt + 2 * KS < n_tiles) issue_tile(kt + 2 * KS, i + 2);
-    if (!(mine && wave_live && kt * kPfTile <= wave_pos_hi)) continue;
-
+    if (has(i + 3)) issue_tile(kt + 3 * KS, i + 3);
+    if (mine && wave_live && kt * kPfTile <= wave_pos_hi) {
+    const unsigned char* const tile = btile(i);
+    const float* const ksc = reinterpret_cast<const float*>(tile + 2 * Tl::kMatBytes);
+    const float* const vsc = ksc + kPfTile;
     const int key0 = kt * kPfTile;
     f32x16_t sc[2];
 #pragma unroll
@@ -311,6 +325,8 @@ __global__ __launch_bounds__(256 * KS) void prefill_i8_kernel(PrefillArgs a) {
                                                        0, 0, 0);
       }
     }
+    }
+    if (has(i + 1)) convert_tile(kt + KS, i + 1);
   }
 
   if constexpr (KS == 2) {
